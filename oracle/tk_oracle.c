@@ -1,0 +1,165 @@
+/*
+ * CPU oracle for the exact row-wise bf16 top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header, table or constant with the HIP library it checks.
+ *
+ * What is computed (TensorFold PR #713 "the drafter's attention and top-k use
+ * more of the GPU", change 3 and the Exactness table):
+ *   - each row's top-k entries in "(score, lower token) order": score
+ *     descending, and among equal scores the lower column index first;
+ *   - per row an entry count and a non-finite mask;
+ *   - the cases that must be exact: ties, both zeros, NaN and infinities, and
+ *     padded row strides.
+ * Readings taken where that page is silent (each is a plain reading):
+ *   - NaN of any sign or payload is never an entry; it sets mask bit 1;
+ *   - +inf and -inf are ranked by value and set mask bits 2 and 4;
+ *   - +0 and -0 compare equal (ties go to the lower column); an entry's value
+ *     is the input's own bit pattern, so a -0 entry stays 0x8000;
+ *   - count = min(k, number of non-NaN columns); entry slots at and past
+ *     count hold index -1 and value 0x7FC0;
+ *   - row_stride is in elements; columns [cols, row_stride) are never read.
+ *
+ * Method: every value is widened exactly to double, non-NaN values are
+ * collected with their column, and the list is sorted with qsort under the
+ * comparison "larger value first, then smaller column first".  Because no two
+ * entries share a column, that comparison is a strict total order and the
+ * sorted list is unique.  The first min(k, n) entries are the answer.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  double value;
+  int32_t col;
+} tko_entry;
+
+/* Exact widening of a bf16 bit pattern: bf16 is the top half of a binary32. */
+static double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* qsort comparator: negative when a comes first in (score desc, column asc). */
+static int score_then_lower_column(const void *pa, const void *pb) {
+  const tko_entry *a = (const tko_entry *)pa;
+  const tko_entry *b = (const tko_entry *)pb;
+  if (a->value > b->value) return -1;
+  if (a->value < b->value) return 1;
+  if (a->col < b->col) return -1;
+  if (a->col > b->col) return 1;
+  return 0;
+}
+
+typedef struct {
+  int64_t row_begin, row_end, cols, row_stride;
+  int32_t k;
+  const uint16_t *in;
+  int32_t *out_idx;
+  uint16_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+  int status;
+} tko_job;
+
+static void *run_rows(void *arg) {
+  tko_job *job = (tko_job *)arg;
+  tko_entry *list = (tko_entry *)malloc((size_t)(job->cols > 0 ? job->cols : 1) * sizeof(tko_entry));
+  if (!list) {
+    job->status = -1;
+    return NULL;
+  }
+  for (int64_t r = job->row_begin; r < job->row_end; ++r) {
+    const uint16_t *row = job->in + r * job->row_stride;
+    uint32_t mask = 0;
+    int64_t n = 0;
+    for (int64_t c = 0; c < job->cols; ++c) {
+      double v = bf16_value(row[c]);
+      if (isnan(v)) {
+        mask |= 1u;
+        continue;
+      }
+      if (isinf(v)) mask |= (v > 0) ? 2u : 4u;
+      list[n].value = v;
+      list[n].col = (int32_t)c;
+      ++n;
+    }
+    qsort(list, (size_t)n, sizeof(tko_entry), score_then_lower_column);
+    int64_t count = n < job->k ? n : job->k;
+    for (int64_t j = 0; j < job->k; ++j) {
+      int64_t o = r * job->k + j;
+      if (j < count) {
+        job->out_idx[o] = list[j].col;
+        job->out_val[o] = row[list[j].col];
+      } else {
+        job->out_idx[o] = -1;
+        job->out_val[o] = 0x7FC0;
+      }
+    }
+    job->out_count[r] = (int32_t)count;
+    job->out_nonfinite[r] = mask;
+  }
+  free(list);
+  job->status = 0;
+  return NULL;
+}
+
+/*
+ * Row-wise top-k of a rows x cols bf16 matrix stored with row_stride elements
+ * between row starts.  Outputs are dense: out_idx/out_val [rows][k],
+ * out_count/out_nonfinite [rows].  Rows are split into contiguous blocks over
+ * `threads` POSIX threads (threads <= 1 runs on the caller's thread).
+ * Returns 0, or -1 for invalid arguments or an allocation failure.
+ */
+int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                  int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                  int32_t threads) {
+  if (rows < 0 || cols < 0 || cols > INT32_MAX || row_stride < cols || k < 1) return -1;
+  if (rows == 0) return 0;
+  if ((cols > 0 && !in) || !out_idx || !out_val || !out_count || !out_nonfinite) return -1;
+  if (threads < 1) threads = 1;
+  if (threads > rows) threads = (int32_t)rows;
+
+  tko_job *jobs = (tko_job *)calloc((size_t)threads, sizeof(tko_job));
+  pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+  if (!jobs || !tids) {
+    free(jobs);
+    free(tids);
+    return -1;
+  }
+  for (int32_t t = 0; t < threads; ++t) {
+    tko_job *j = &jobs[t];
+    j->row_begin = rows * t / threads;
+    j->row_end = rows * (t + 1) / threads;
+    j->cols = cols;
+    j->row_stride = row_stride;
+    j->k = k;
+    j->in = in;
+    j->out_idx = out_idx;
+    j->out_val = out_val;
+    j->out_count = out_count;
+    j->out_nonfinite = out_nonfinite;
+    j->status = -1;
+  }
+  int started = 0;
+  for (int32_t t = 1; t < threads; ++t) {
+    if (pthread_create(&tids[t], NULL, run_rows, &jobs[t]) != 0) break;
+    started = t;
+  }
+  run_rows(&jobs[0]);
+  /* rows of threads that could not start run here, in order */
+  for (int32_t t = started + 1; t < threads; ++t) run_rows(&jobs[t]);
+  for (int32_t t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+  int status = 0;
+  for (int32_t t = 0; t < threads; ++t)
+    if (jobs[t].status != 0) status = -1;
+  free(jobs);
+  free(tids);
+  return status;
+}
