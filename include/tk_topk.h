@@ -1,0 +1,124 @@
+/*
+ * tk_topk.h -- exact row-wise top-k over wide bf16 rows on AMD Instinct MI355X.
+ *
+ * The operation (TensorFold PR #713 "the drafter's attention and top-k use
+ * more of the GPU", change 3 and its Exactness table): for every row of a
+ * rows x cols matrix of bf16 logits, return the k best entries in
+ * "(score, lower token) order" -- score descending, and among equal scores the
+ * lower column index first -- together with the row's entry count and a
+ * non-finite mask.  Results must be byte-equal across every way the work is
+ * split (the page compares its span path with a single-group control) and to
+ * a CPU oracle, over ties, both zeros, NaN, infinities and padded strides.
+ *
+ * Value policy (plain readings where the page is silent):
+ *   NaN   -- any sign or payload; never an entry; sets TK_NONFINITE_NAN.
+ *   +inf  -- ranked as the largest value; sets TK_NONFINITE_POSINF.
+ *   -inf  -- ranked as the smallest value; sets TK_NONFINITE_NEGINF.
+ *   +0/-0 -- compare equal (the lower column wins); each entry keeps its own
+ *            bit pattern, so a -0 entry is 0x8000.
+ *   subnormals are ordered by exact value (nothing is flushed).
+ *
+ * Layouts (all device memory, owned by the caller):
+ *   in             rows x row_stride bf16 bit patterns, row-major, row_stride
+ *                  in ELEMENTS; only columns [0, cols) of each row are read,
+ *                  the padding [cols, row_stride) is never touched.
+ *   out_idx        int32  [rows][k]  column of entry j (0 <= j < count), else -1
+ *   out_val        uint16 [rows][k]  bf16 bits of in[r][out_idx], else 0x7FC0
+ *   out_count      int32  [rows]     min(k, number of non-NaN columns of the row)
+ *   out_nonfinite  uint32 [rows]     OR of TK_NONFINITE_* over the row's columns
+ *
+ * Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream): outputs are valid once the stream passes the call.  The library
+ * keeps no pointer after the call returns; the caller keeps the buffers alive
+ * until the stream has passed the call.  Calls on different streams may run
+ * concurrently.  Temporary span lists are stream-ordered allocations of the
+ * library (hipMallocAsync / hipFreeAsync on `stream`).
+ *
+ * Errors: the guards below run on the host before any device work; on a
+ * guard error nothing is launched and nothing is written.  TK_ERR_DEVICE
+ * reports a failed allocation or launch; an asynchronous fault surfaces at the
+ * caller's next synchronisation (HIP convention).
+ */
+#ifndef TK_TOPK_H
+#define TK_TOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TK_MAX_K 64u /* largest k; one wavefront lane per kept entry */
+
+#define TK_NONFINITE_NAN 1u    /* the row has at least one NaN (none is an entry)  */
+#define TK_NONFINITE_POSINF 2u /* the row has at least one +inf                    */
+#define TK_NONFINITE_NEGINF 4u /* the row has at least one -inf                    */
+
+#define TK_FILL_IDX (-1)      /* out_idx of an unused entry slot */
+#define TK_FILL_VAL 0x7FC0u   /* out_val of an unused entry slot (a quiet NaN) */
+
+typedef enum tk_status {
+  TK_OK = 0,
+  TK_ERR_NULL = 1,   /* a required pointer is NULL (rows > 0) */
+  TK_ERR_SHAPE = 2,  /* rows < 0, cols < 0, cols > INT32_MAX, row_stride < cols, or sizes overflow */
+  TK_ERR_K = 3,      /* k < 1 or k > TK_MAX_K */
+  TK_ERR_ALIGN = 4,  /* in/out_val not 2-byte aligned, or out_idx/out_count/out_nonfinite not 4-byte aligned */
+  TK_ERR_ALIAS = 5,  /* two of the five buffers overlap (outputs must not alias the input or each other) */
+  TK_ERR_DEVICE = 6, /* HIP reported an error while allocating or launching */
+  TK_ERR_OPTION = 7  /* tk_options out of range */
+} tk_status;
+
+/*
+ * Row-wise exact top-k (see the file comment for the contract).
+ *   rows        >= 0; rows == 0 returns TK_OK without touching the device.
+ *   cols        0 <= cols <= INT32_MAX; cols == 0 gives count 0 and all fills.
+ *   row_stride  >= cols, in elements.
+ *   k           1 <= k <= TK_MAX_K; k may exceed cols.
+ *   stream      hipStream_t the work is queued on.
+ */
+tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                       int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                       void *stream);
+
+/*
+ * Planning overrides, for tests and benchmarks.  The result never depends on
+ * them: every plan computes the same bytes.
+ *   spans  0 = automatic; 1 = one workgroup scans each whole row (the
+ *          single-group control); n > 1 = split each row into n spans whose
+ *          candidate lists a second dispatch merges.  Rejected with
+ *          TK_ERR_OPTION when a span would exceed the library's span limit
+ *          (tk_max_span_cols()) or n > cols (for cols > 0).
+ */
+typedef struct tk_options {
+  int32_t spans;
+  int32_t reserved[7]; /* must be zero */
+} tk_options;
+
+tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                          int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                          void *stream, const tk_options *opt);
+
+/*
+ * The host-side guards alone (no HIP call is made): returns the status
+ * tk_topk_bf16 would return before launching anything.
+ */
+tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                           const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
+                           const uint32_t *out_nonfinite);
+
+/*
+ * The span count the automatic plan picks for a shape on a GPU with
+ * `compute_units` CUs (host-only arithmetic; no HIP call).
+ */
+int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units);
+
+int32_t tk_max_k(void);             /* == TK_MAX_K */
+int64_t tk_max_span_cols(void);     /* widest span one workgroup scans */
+const char *tk_status_string(tk_status s);
+const char *tk_build_info(void);    /* target and build flags of the library */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TK_TOPK_H */

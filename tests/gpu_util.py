@@ -1,0 +1,77 @@
+"""Helpers for the GPU tests: upload seeded inputs, call the C ABI through the
+binding, and compare with the CPU oracle byte for byte."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+POISON_WORD = 0x7FC0
+
+
+def need_gpu():
+    import pytest
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upload(m: np.ndarray, offset: int = 0):
+    """Copies a (rows, stride) uint16 matrix to the device.  With offset > 0 the
+    rows start `offset` elements past a fresh allocation (misaligned rows); the
+    elements before them hold NaN poison."""
+    import torch
+
+    rows, stride = m.shape
+    base = torch.empty(offset + rows * stride, dtype=torch.int16, device="cuda")
+    if offset:
+        base[:offset] = np.int16(np.uint16(POISON_WORD).view(np.int16))
+    if rows * stride:
+        base[offset:] = torch.from_numpy(np.ascontiguousarray(m).view(np.int16).reshape(-1)).to("cuda")
+    return base[offset:].view(rows, stride)
+
+
+def to_numpy(out):
+    import torch
+
+    torch.cuda.synchronize()
+    return (
+        out.idx.cpu().numpy(),
+        out.val.view(torch.int16).cpu().numpy().view(np.uint16),
+        out.count.cpu().numpy(),
+        out.nonfinite.cpu().numpy().view(np.uint32),
+    )
+
+
+def gpu_topk(m: np.ndarray, cols: int, k: int, spans: int = 0, offset: int = 0, x=None):
+    import wide_row_bf16_amd as tk
+
+    x = upload(m, offset) if x is None else x
+    return to_numpy(tk.topk_bf16(x, k, cols=cols, spans=spans))
+
+
+def assert_same(got, want, what: str):
+    names = ("idx", "val", "count", "nonfinite")
+    for g, w, n in zip(got, want, names):
+        if not np.array_equal(g, w):
+            bad = np.argwhere(g != w)
+            first = tuple(bad[0])
+            raise AssertionError(
+                f"{what}: {n} differs at {len(bad)} places, first {first}: got {g[first]} want {w[first]}"
+            )
+
+
+def check_case(m, cols, k, spans=0, offset=0, what="", want=None):
+    want = oracle.topk_bf16(m, cols, k) if want is None else want
+    got = gpu_topk(m, cols, k, spans=spans, offset=offset)
+    assert_same(got, want, what or f"cols={cols} k={k} spans={spans} offset={offset}")
+    return got

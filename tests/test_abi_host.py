@@ -1,0 +1,119 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+and its guards reject bad arguments before any HIP call (CPU only)."""
+
+import os
+import re
+
+import pytest
+
+import wide_row_bf16_amd as tk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tk_topk.h")
+
+OK, NULL, SHAPE, K, ALIGN, ALIAS, DEVICE, OPTION = range(8)
+
+# Fake, well-separated, aligned device addresses: the guards only do arithmetic on them.
+IN, IDX, VAL, CNT, MSK = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(tk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tk.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_constants():
+    text = open(HEADER).read()
+    assert tk.max_k() == int(re.search(r"#define TK_MAX_K (\d+)u", text).group(1)) == 64
+    assert tk.max_span_cols() >= 4 * 65000
+    assert b"gfx950" in tk.load().tk_build_info()
+    for s in range(8):
+        assert tk.load().tk_status_string(s)
+
+
+def v(rows=4, cols=100, stride=100, k=8, i=IN, o=IDX, val=VAL, c=CNT, m=MSK):
+    return tk.validate(rows, cols, stride, k, i, o, val, c, m)
+
+
+def test_guard_accepts_valid_calls():
+    assert v() == OK
+    assert v(rows=0, i=None, o=None, val=None, c=None, m=None) == OK  # empty: nothing is touched
+    assert v(cols=0, stride=0) == OK
+    assert v(k=64) == OK and v(k=1) == OK
+    assert v(k=64, cols=3, stride=3) == OK  # k may exceed cols
+    assert v(i=IN + 2, val=VAL + 2) == OK    # 2-byte alignment is enough for bf16 buffers
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(rows=-1), SHAPE),
+        (dict(cols=-1), SHAPE),
+        (dict(cols=2**31, stride=2**31), SHAPE),
+        (dict(stride=99), SHAPE),
+        (dict(rows=2**40, stride=2**40), SHAPE),
+        (dict(k=0), K),
+        (dict(k=65), K),
+        (dict(k=-3), K),
+        (dict(i=None), NULL),
+        (dict(o=None), NULL),
+        (dict(val=None), NULL),
+        (dict(c=None), NULL),
+        (dict(m=None), NULL),
+        (dict(i=IN + 1), ALIGN),
+        (dict(val=VAL + 1), ALIGN),
+        (dict(o=IDX + 2), ALIGN),
+        (dict(c=CNT + 2), ALIGN),
+        (dict(m=MSK + 1), ALIGN),
+        (dict(o=IN + 64), ALIAS),                # output inside the input span
+        (dict(val=IDX + 4 * 4 * 8 - 2), ALIAS),  # val overlaps the tail of idx
+        (dict(c=MSK), ALIAS),                    # count and mask share storage
+        (dict(m=IN + 2 * (3 * 100 + 100) - 4), ALIAS),  # mask overlaps the last input row
+    ],
+)
+def test_guard_rejects(kw, status):
+    assert v(**kw) == status
+
+
+def test_guard_ignores_padding_when_cols_zero():
+    # with cols == 0 nothing of the input is read, so nothing can alias it
+    assert v(cols=0, stride=0, o=IN) == OK
+
+
+def test_plan():
+    assert tk.plan_spans(1024, 151936, 64) == 1      # enough rows for every CU
+    assert tk.plan_spans(15, 98592, 32) > 1          # few rows: split
+    assert tk.plan_spans(1, 4096, 8) == 1            # too narrow to split
+    assert tk.plan_spans(4, 10**7, 8) >= (10**7 // 8 + 32639) // 32640  # span width limit
+    assert tk.plan_spans(100000, 10**6, 8) >= 4
+    for rows in (1, 3, 15, 64, 255, 256, 1000):
+        for cols in (0, 1, 4095, 4096, 70000, 151936, 248320, 600000):
+            s = tk.plan_spans(rows, cols, 16)
+            assert 1 <= s and (cols // 8 + s - 1) // s <= tk.max_span_cols() // 8
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle and the HIP path are built from disjoint sources."""
+    import oracle
+
+    src = open(oracle.SOURCE).read()
+    assert "#include \"" not in src  # only system headers
+    for name in os.listdir(os.path.join(ROOT, "wide_row_bf16_amd", "csrc")):
+        assert name not in src
+    for root, _, files in os.walk(os.path.join(ROOT, "wide_row_bf16_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "tk_oracle" not in text, f

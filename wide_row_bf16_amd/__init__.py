@@ -1,0 +1,165 @@
+"""Exact row-wise bf16 top-k on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/tk_topk.h``: it checks
+tensor metadata, allocates the four outputs with PyTorch and passes raw
+device pointers and the current HIP stream to ``libtk_topk.so``.  Every step
+of the top-k runs in that library's HIP kernels; there is no other path.
+
+    idx, val, count, nonfinite = topk_bf16(logits, k)
+
+``logits`` is a 2-D bf16 CUDA (HIP) tensor whose last dimension is
+contiguous (any row stride >= its width).  Results: ``idx`` int32 [rows, k]
+(column of each entry, -1 past ``count``), ``val`` bf16 [rows, k] (the
+entry's own bits; 0x7FC0 past ``count``), ``count`` int32 [rows], and
+``nonfinite`` int32 [rows] holding the mask bits NAN=1, POSINF=2, NEGINF=4.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libtk_topk.so")
+
+TK_OK = 0
+STATUS_NAMES = {
+    0: "TK_OK", 1: "TK_ERR_NULL", 2: "TK_ERR_SHAPE", 3: "TK_ERR_K", 4: "TK_ERR_ALIGN",
+    5: "TK_ERR_ALIAS", 6: "TK_ERR_DEVICE", 7: "TK_ERR_OPTION",
+}
+NONFINITE_NAN, NONFINITE_POSINF, NONFINITE_NEGINF = 1, 2, 4
+FILL_IDX, FILL_VAL = -1, 0x7FC0
+
+# Every symbol the public header declares.
+EXPORTS = (
+    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_validate_bf16", "tk_plan_spans", "tk_max_k",
+    "tk_max_span_cols", "tk_status_string", "tk_build_info",
+)
+
+
+class TkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({_status_string(status)})")
+
+
+class TkOptions(ctypes.Structure):
+    _fields_ = [("spans", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class TopK(NamedTuple):
+    idx: "object"
+    val: "object"
+    count: "object"
+    nonfinite: "object"
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libtk_topk.so, compiling it with hipcc first only if it is not built."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        if path != LIBRARY:
+            raise FileNotFoundError(path)
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.tk_topk_bf16.restype = i32
+    lib.tk_topk_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.tk_topk_bf16_ex.restype = i32
+    lib.tk_topk_bf16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
+    lib.tk_validate_bf16.restype = i32
+    lib.tk_validate_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.tk_plan_spans.restype = i32
+    lib.tk_plan_spans.argtypes = [i64, i64, i32, i32]
+    lib.tk_max_k.restype = i32
+    lib.tk_max_k.argtypes = []
+    lib.tk_max_span_cols.restype = i64
+    lib.tk_max_span_cols.argtypes = []
+    lib.tk_status_string.restype = ctypes.c_char_p
+    lib.tk_status_string.argtypes = [i32]
+    lib.tk_build_info.restype = ctypes.c_char_p
+    lib.tk_build_info.argtypes = []
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load().tk_status_string(status).decode()
+    except OSError:
+        return "?"
+
+
+def max_k() -> int:
+    return int(load().tk_max_k())
+
+
+def max_span_cols() -> int:
+    return int(load().tk_max_span_cols())
+
+
+def plan_spans(rows: int, cols: int, k: int, compute_units: int = 256) -> int:
+    return int(load().tk_plan_spans(rows, cols, k, compute_units))
+
+
+def validate(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr) -> int:
+    """The host-side guards on raw pointers (no HIP call); returns a status code."""
+    return int(load().tk_validate_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr))
+
+
+def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream=0, spans=0) -> int:
+    """Calls the C ABI on raw device pointers; returns the status code."""
+    lib = load()
+    if spans:
+        opt = TkOptions(spans=spans)
+        return int(lib.tk_topk_bf16_ex(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
+                                       stream, ctypes.byref(opt)))
+    return int(lib.tk_topk_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
+
+
+def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, out: TopK | None = None, stream=None) -> TopK:
+    """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
+
+    ``cols`` limits the scan to the first ``cols`` columns (default: all);
+    ``spans`` forces the row split (0 = automatic, 1 = one workgroup per row);
+    ``out`` reuses preallocated outputs; ``stream`` is a torch.cuda.Stream
+    (default: the current stream).
+    """
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected bf16 bit patterns, got {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError("expected a tensor on a HIP device")
+    rows, width = x.shape
+    if rows > 0 and width > 0 and x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    cols = width if cols is None else cols
+    if cols > width:
+        raise ValueError("cols exceeds the tensor width")
+    row_stride = x.stride(0) if rows > 1 else max(cols, 1)
+    if out is None:
+        out = TopK(
+            torch.empty((rows, k), dtype=torch.int32, device=x.device),
+            torch.empty((rows, k), dtype=torch.bfloat16, device=x.device),
+            torch.empty((rows,), dtype=torch.int32, device=x.device),
+            torch.empty((rows,), dtype=torch.int32, device=x.device),
+        )
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        status = topk_bf16_raw(rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(),
+                               out.count.data_ptr(), out.nonfinite.data_ptr(), st.cuda_stream, spans)
+    if status != TK_OK:
+        raise TkError(status, "tk_topk_bf16")
+    return out

@@ -1,0 +1,267 @@
+// C ABI of the wide-row bf16 top-k library: host guards, span planning,
+// stream-ordered scratch and kernel launches.  Contract: include/tk_topk.h.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <limits>
+
+#include "tk_config.h"
+#include "tk_launch.h"
+
+#ifndef TK_BUILD_INFO
+#define TK_BUILD_INFO "unknown build"
+#endif
+
+namespace {
+
+using tk::kMaxK;
+using tk::kMaxSpanVecs;
+using tk::kMergeGroup;
+using tk::kVecElems;
+
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;  // keeps grid work-items below 2^32
+constexpr int64_t kMinSpanCols = 4096;                      // a split never makes spans narrower
+constexpr int32_t kMaxAutoSpans = 64;                       // automatic plans fold in one merge level
+constexpr int32_t kMaxSpans = 1 << 16;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi), empty when lo == hi
+};
+
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
+
+tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const void *in, const void *out_idx,
+                const void *out_val, const void *out_count, const void *out_nonfinite) {
+  if (rows < 0 || cols < 0 || cols > INT32_MAX || stride < cols) return TK_ERR_SHAPE;
+  if (k < 1 || k > kMaxK) return TK_ERR_K;
+  if (rows == 0) return TK_OK;
+  if (!in || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;
+  const int64_t big = std::numeric_limits<int64_t>::max() / 8;
+  if (!mul_ok(rows - 1, stride, big) || (rows - 1) * stride > big - cols) return TK_ERR_SHAPE;
+  if (!mul_ok(rows, k, big)) return TK_ERR_SHAPE;
+  if (((uintptr_t)in & 1) || ((uintptr_t)out_val & 1)) return TK_ERR_ALIGN;
+  if (((uintptr_t)out_idx & 3) || ((uintptr_t)out_count & 3) || ((uintptr_t)out_nonfinite & 3)) return TK_ERR_ALIGN;
+  const int64_t in_elems = cols > 0 ? (rows - 1) * stride + cols : 0;
+  const Range rs[5] = {
+      {(uintptr_t)in, (uintptr_t)in + (uintptr_t)(2 * in_elems)},
+      {(uintptr_t)out_idx, (uintptr_t)out_idx + (uintptr_t)(4 * rows * k)},
+      {(uintptr_t)out_val, (uintptr_t)out_val + (uintptr_t)(2 * rows * k)},
+      {(uintptr_t)out_count, (uintptr_t)out_count + (uintptr_t)(4 * rows)},
+      {(uintptr_t)out_nonfinite, (uintptr_t)out_nonfinite + (uintptr_t)(4 * rows)},
+  };
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(rs[i], rs[j])) return TK_ERR_ALIAS;
+  return TK_OK;
+}
+
+// Smallest span count that keeps every span within one workgroup's limit.
+int64_t min_spans(int64_t cols) {
+  const int64_t nv = cols / kVecElems;
+  const int64_t s = (nv + kMaxSpanVecs - 1) / kMaxSpanVecs;
+  return s < 1 ? 1 : s;
+}
+
+int32_t plan(int64_t rows, int64_t cols, int32_t compute_units) {
+  if (cols <= 0 || rows <= 0) return 1;
+  const int64_t need = min_spans(cols);
+  int64_t s = 1;
+  if (rows < compute_units) {
+    // Few rows: split each row so that rows * spans covers every CU once,
+    // without making spans narrower than kMinSpanCols.
+    s = (compute_units + rows - 1) / rows;
+    const int64_t by_width = cols / kMinSpanCols;
+    if (s > by_width) s = by_width;
+    if (s > kMaxAutoSpans) s = kMaxAutoSpans;
+  }
+  if (s < need) s = need;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+std::atomic<int32_t> g_cu_count[64];
+std::atomic<bool> g_pool_ready[64];
+
+int32_t device_cus(int dev) {
+  if (dev < 0 || dev >= 64) return 256;
+  int32_t v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Keep stream-ordered allocations in the device's default pool between calls.
+void keep_pool(int dev) {
+  if (dev < 0 || dev >= 64 || g_pool_ready[dev].load(std::memory_order_acquire)) return;
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    uint64_t threshold = std::numeric_limits<uint64_t>::max();
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+  }
+  g_pool_ready[dev].store(true, std::memory_order_release);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
+              uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
+              const tk_options *opt) {
+  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
+  if (st != TK_OK) return st;
+  int32_t forced = 0;
+  if (opt) {
+    for (int i = 0; i < 7; ++i)
+      if (opt->reserved[i] != 0) return TK_ERR_OPTION;
+    forced = opt->spans;
+    if (forced < 0 || forced > kMaxSpans) return TK_ERR_OPTION;
+    if (forced > 1 && cols > 0 && forced > cols) return TK_ERR_OPTION;
+    if (forced >= 1 && forced < min_spans(cols)) return TK_ERR_OPTION;
+  }
+  if (rows == 0) return TK_OK;
+
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  const int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
+
+  tk::ScanArgs sa{};
+  sa.in = in;
+  sa.cols = cols;
+  sa.stride = stride;
+  sa.k = k;
+  sa.spans = spans;
+  sa.out_idx = out_idx;
+  sa.out_val = out_val;
+  sa.out_count = out_count;
+  sa.out_nonfinite = out_nonfinite;
+
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
+  if (spans == 1) {
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+      const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+      sa.row0 = r0;
+      if (tk::launch_span_scan(sa, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
+    }
+    return TK_OK;
+  }
+
+  // Scratch for one batch of rows: the span lists, then each merge level's lists.
+  const int64_t batch = rows < rows_per_launch ? rows : rows_per_launch;
+  int32_t level_lists[8];
+  int levels = 0;
+  for (int32_t n = spans; n > 1; n = (n + kMergeGroup - 1) / kMergeGroup) level_lists[levels++] = n;
+  size_t off_list[8], off_count[8], off_flags[8], total = 0;
+  for (int i = 0; i < levels; ++i) {
+    const size_t nlists = (size_t)batch * (size_t)level_lists[i];
+    off_list[i] = total;
+    total = align256(total + nlists * (size_t)k * sizeof(uint64_t));
+    off_count[i] = total;
+    total = align256(total + nlists * sizeof(int32_t));
+    off_flags[i] = total;
+    total = align256(total + nlists * sizeof(uint32_t));
+  }
+  keep_pool(dev);
+  void *scratch = nullptr;
+  if (hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
+  char *base = (char *)scratch;
+
+  tk_status result = TK_OK;
+  for (int64_t r0 = 0; r0 < rows && result == TK_OK; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    // Scratch rows are indexed from the batch start: point the row-indexed
+    // outputs of the scan at the batch, and offset the input by r0 rows.
+    tk::ScanArgs b = sa;
+    b.in = in + r0 * stride;
+    b.row0 = 0;
+    b.span_list = (uint64_t *)(base + off_list[0]);
+    b.span_count = (int32_t *)(base + off_count[0]);
+    b.span_flags = (uint32_t *)(base + off_flags[0]);
+    if (tk::launch_span_scan(b, nr, stream) != hipSuccess) {
+      result = TK_ERR_DEVICE;
+      break;
+    }
+    for (int i = 0; i < levels; ++i) {
+      tk::MergeArgs m{};
+      m.in = in + r0 * stride;
+      m.row0 = 0;
+      m.stride = stride;
+      m.k = k;
+      m.lists_in = level_lists[i];
+      m.group = level_lists[i] < kMergeGroup ? level_lists[i] : kMergeGroup;
+      m.lists_out = (level_lists[i] + m.group - 1) / m.group;
+      m.list_in = (const uint64_t *)(base + off_list[i]);
+      m.count_in = (const int32_t *)(base + off_count[i]);
+      m.flags_in = (const uint32_t *)(base + off_flags[i]);
+      if (i + 1 < levels) {
+        m.list_out = (uint64_t *)(base + off_list[i + 1]);
+        m.count_out = (int32_t *)(base + off_count[i + 1]);
+        m.flags_out = (uint32_t *)(base + off_flags[i + 1]);
+      } else {
+        m.out_idx = out_idx + r0 * k;
+        m.out_val = out_val + r0 * k;
+        m.out_count = out_count + r0;
+        m.out_nonfinite = out_nonfinite + r0;
+      }
+      if (tk::launch_span_merge(m, nr, stream) != hipSuccess) {
+        result = TK_ERR_DEVICE;
+        break;
+      }
+    }
+  }
+  if (hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  return result;
+}
+
+}  // namespace
+
+extern "C" {
+
+tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                       int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                       void *stream) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr);
+}
+
+tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                          int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                          void *stream, const tk_options *opt) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, opt);
+}
+
+tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                           const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
+                           const uint32_t *out_nonfinite) {
+  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite);
+}
+
+int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
+  (void)k;
+  return plan(rows, cols, compute_units > 0 ? compute_units : 256);
+}
+
+int32_t tk_max_k(void) { return kMaxK; }
+
+int64_t tk_max_span_cols(void) { return tk::kMaxSpanCols; }
+
+const char *tk_status_string(tk_status s) {
+  switch (s) {
+    case TK_OK: return "ok";
+    case TK_ERR_NULL: return "a required pointer is NULL";
+    case TK_ERR_SHAPE: return "invalid shape (rows, cols or row_stride)";
+    case TK_ERR_K: return "k out of range [1, TK_MAX_K]";
+    case TK_ERR_ALIGN: return "misaligned buffer";
+    case TK_ERR_ALIAS: return "buffers overlap";
+    case TK_ERR_DEVICE: return "HIP error while allocating or launching";
+    case TK_ERR_OPTION: return "invalid tk_options";
+  }
+  return "unknown status";
+}
+
+const char *tk_build_info(void) { return TK_BUILD_INFO; }
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Compile-time constants of the top-k library, shared by its kernels and its
+// host code.  Tying them together here (with static_asserts) means a change to
+// one of them fails the build instead of a merge -- the same protection the
+// TensorFold PR #713 change 3 describes for its lane, span and max_k constants.
+#pragma once
+
+#include <stdint.h>
+
+#include "tk_topk.h"
+
+namespace tk {
+
+constexpr int kWave = 64;                      // CDNA wavefront width
+constexpr int kWgWaves = 4;                    // waves per scan workgroup
+constexpr int kWgThreads = kWave * kWgWaves;   // 256
+constexpr int kMaxK = 64;                      // kept entries: one per lane
+constexpr int kVecElems = 8;                   // bf16 per 16-byte load
+constexpr int kChunkVecs = 4;                  // 16-byte loads per lane per chunk
+constexpr int64_t kMaxWaveCols = 65536;        // a wave's relative column fits 16 bits
+constexpr int64_t kMaxSpanVecs = 32640;        // 16-byte vectors one workgroup scans at most
+constexpr int64_t kMaxSpanCols = kMaxSpanVecs * kVecElems;  // 261120
+constexpr int kMergeGroup = 64;                // span lists one merge workgroup folds at most
+constexpr int kMergeThreads = 256;
+constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
+
+static_assert(kMaxK == (int)TK_MAX_K, "public and internal max k differ");
+static_assert(kMaxK <= kWave, "a wave holds one kept entry per lane");
+static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
+// A wave scans at most ceil(kMaxSpanVecs / kWgWaves) vectors plus two partial
+// edges of < kVecElems columns each; its columns must stay within 16 bits.
+static_assert(((kMaxSpanVecs + kWgWaves - 1) / kWgWaves) * kVecElems + 2 * kVecElems <= kMaxWaveCols,
+              "a wave's column range must fit the 16-bit relative index");
+static_assert(kMergeGroup * kMaxK * 8 * 2 <= 64 * 1024, "merge double buffer must fit LDS");
+
+}  // namespace tk

@@ -1,0 +1,625 @@
+// Exact row-wise bf16 top-k kernels for CDNA4 (gfx950).
+//
+// What is computed (TensorFold PR #713 "the drafter's attention and top-k use
+// more of the GPU", change 3): each row's k best entries in "(score, lower
+// token) order".  Wide rows may be split into spans whose candidate lists a
+// second dispatch merges "with the same tournament and the same (score, lower
+// token) order"; the result must not depend on the split (Exactness table of
+// the same page).
+//
+// Order key.  A bf16 pattern b with magnitude m = b & 0x7FFF maps to the
+// 16-bit key 0x8000 + m (sign clear) or 0x8000 - m (sign set).  The key is
+// monotone in value, gives +0 and -0 the same key 0x8000, keeps subnormals
+// in order, and sends -inf to 0x0080 and +inf to 0xFF80.  NaN (m > 0x7F80)
+// gets key 0, below every number, and is never kept.  Inside one wave the
+// composite (key << 16) | (0xFFFF - rel), rel = column - wave base < 65536,
+// is a strict total order equal to (score desc, column asc); across waves and
+// spans the 64-bit composite (key << 32) | (0xFFFFFFFF - column) is used.
+//
+// Scan (one workgroup = four wave64s per (row, span)).  Each wave streams its
+// contiguous share of the span with 16-byte loads (64 lanes x 16 B = 1 KiB per
+// load instruction, four per lane per chunk, double buffered) and keeps the 64
+// best composites seen so far in one VGPR, lane i holding the i-th best.  Let
+// T be the k-th kept key.  A wave visits its columns in increasing order, so a
+// later element that only ties T loses to it (lower column wins): the filter
+// "key > T" is exact.  It is evaluated on raw bf16 bits with two packed 16-bit
+// operations per dword: for T >= 0 an element beats T iff its bits, read as
+// int16, exceed T's magnitude; for T < 0 iff its bits, read as uint16, are
+// below T's bits.  A per-lane packed uint16 max also catches -inf and NaN
+// patterns the wave has not flagged yet.  Only when some lane trips does the
+// wave take the exact path: keys and composites per element, a 19-comparator
+// sort of the lane's eight, and insertion position by position -- one DPP
+// wave_shr per new entry when few lanes have one, a bitonic sort and merge of
+// 64 when many do.
+//
+// Merge.  The four wave lists meet in LDS; every candidate finds its rank by
+// binary search in the other lists and writes itself at that rank.  With
+// several spans per row, the span lists go to memory and a second kernel folds
+// them pairwise in LDS (a tournament) with the same rank rule.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tk_config.h"
+#include "tk_launch.h"
+
+namespace tk {
+namespace {
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kNan = TK_NONFINITE_NAN;
+constexpr uint32_t kPinf = TK_NONFINITE_POSINF;
+constexpr uint32_t kNinf = TK_NONFINITE_NEGINF;
+constexpr uint32_t kKeyPosInf = 0xFF80u;
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// v from lane (lane ^ MASK).
+template <int MASK>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  static_assert(MASK > 0 && MASK < 64, "lane mask");
+  if constexpr (MASK == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (MASK == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (MASK < 32) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (MASK << 10));  // xor within 32 lanes
+  } else if constexpr (MASK == 32) {
+    return (uint32_t)__shfl_xor((int)v, 32);
+  } else {
+    return xor_lane<32>(xor_lane<MASK - 32>(v));
+  }
+}
+
+// One compare-exchange stage of a bitonic network over the 64 lanes.  Blocks
+// of SIZE lanes alternate direction so that the final SIZE == 64 stage sorts
+// descending.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_stage(uint32_t x) {
+  const uint32_t y = xor_lane<STRIDE>(x);
+  const int l = lane_id();
+  const bool ascending_block = (SIZE < 64) && (l & SIZE);
+  const bool lower = !(l & STRIDE);
+  return (lower != ascending_block) ? max(x, y) : min(x, y);
+}
+
+__device__ __forceinline__ uint32_t sort64_desc(uint32_t x) {
+  x = bitonic_stage<2, 1>(x);
+  x = bitonic_stage<4, 2>(x);
+  x = bitonic_stage<4, 1>(x);
+  x = bitonic_stage<8, 4>(x);
+  x = bitonic_stage<8, 2>(x);
+  x = bitonic_stage<8, 1>(x);
+  x = bitonic_stage<16, 8>(x);
+  x = bitonic_stage<16, 4>(x);
+  x = bitonic_stage<16, 2>(x);
+  x = bitonic_stage<16, 1>(x);
+  x = bitonic_stage<32, 16>(x);
+  x = bitonic_stage<32, 8>(x);
+  x = bitonic_stage<32, 4>(x);
+  x = bitonic_stage<32, 2>(x);
+  x = bitonic_stage<32, 1>(x);
+  x = bitonic_stage<64, 32>(x);
+  x = bitonic_stage<64, 16>(x);
+  x = bitonic_stage<64, 8>(x);
+  x = bitonic_stage<64, 4>(x);
+  x = bitonic_stage<64, 2>(x);
+  x = bitonic_stage<64, 1>(x);
+  return x;
+}
+
+// Sorts a bitonic sequence over the 64 lanes into descending order.
+__device__ __forceinline__ uint32_t bitonic_merge64_desc(uint32_t x) {
+  x = bitonic_stage<64, 32>(x);
+  x = bitonic_stage<64, 16>(x);
+  x = bitonic_stage<64, 8>(x);
+  x = bitonic_stage<64, 4>(x);
+  x = bitonic_stage<64, 2>(x);
+  x = bitonic_stage<64, 1>(x);
+  return x;
+}
+
+// The 64 best of (list, x): sort x, reverse it against the descending list,
+// keep the lane-wise maximum (a bitonic sequence holding the 64 best of the
+// union) and sort that.
+__device__ __forceinline__ uint32_t merge_batch(uint32_t list, uint32_t x) {
+  x = xor_lane<63>(sort64_desc(x));
+  return bitonic_merge64_desc(max(list, x));
+}
+
+// Inserts one composite c into the descending list: lanes before its place
+// keep their entry, lanes from its place on take the previous lane's entry,
+// and its own lane takes c.  list[lane - 1] arrives by DPP wave_shr:1; lane 0
+// reads all-ones so that it keeps max(list[0], c).
+__device__ __forceinline__ uint32_t insert_one(uint32_t list, uint32_t c) {
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)list, 0x138, 0xF, 0xF, false);
+  return max(list, min(prev, c));
+}
+
+__device__ __forceinline__ void cx(uint32_t &a, uint32_t &b) {  // a <- max, b <- min
+  const uint32_t hi = max(a, b);
+  b = min(a, b);
+  a = hi;
+}
+
+// Descending sort of eight values (a 19-comparator network).
+__device__ __forceinline__ void sort8_desc(uint32_t (&c)[8]) {
+  cx(c[0], c[2]); cx(c[1], c[3]); cx(c[4], c[6]); cx(c[5], c[7]);
+  cx(c[0], c[4]); cx(c[1], c[5]); cx(c[2], c[6]); cx(c[3], c[7]);
+  cx(c[0], c[1]); cx(c[2], c[3]); cx(c[4], c[5]); cx(c[6], c[7]);
+  cx(c[2], c[4]); cx(c[3], c[5]);
+  cx(c[1], c[4]); cx(c[3], c[6]);
+  cx(c[1], c[2]); cx(c[3], c[4]); cx(c[5], c[6]);
+}
+
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  const uint32_t mag = b & 0x7FFFu;
+  const uint32_t key = (b & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+  return mag > 0x7F80u ? 0u : key;
+}
+
+struct WaveTopK {
+  uint32_t list;   // lane i: i-th best composite so far, 0 = empty
+  uint32_t kth;    // wave-uniform copy of list[k - 1]
+  uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
+  int km1;         // k - 1
+};
+
+// Adds candidates c (one per lane, 0 = none) whose composite beats the k-th.
+__device__ __forceinline__ void offer(WaveTopK &w, uint32_t c) {
+  uint64_t m = ballot(c > w.kth);
+  if (!m) return;
+  if (__popcll(m) >= kBatchInsert) {
+    w.list = merge_batch(w.list, c > w.kth ? c : 0u);
+  } else {
+    do {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint32_t one = readlane(c, l);
+      if (one > w.kth) {
+        w.list = insert_one(w.list, one);
+        w.kth = readlane(w.list, w.km1);
+      }
+    } while (m);
+  }
+  w.kth = readlane(w.list, w.km1);
+}
+
+// One element whose bits b (wave-uniform) may beat the k-th or carry an
+// unflagged -inf / NaN; inv = 0xFFFF - (column - wave base).
+__device__ __forceinline__ void take_one(WaveTopK &w, uint32_t b, uint32_t inv) {
+  if ((b & 0x7FFFu) > 0x7F80u) {
+    w.flags |= kNan;
+    return;
+  }
+  if (b == 0xFF80u) w.flags |= kNinf;
+  const uint32_t c = (order_key(b) << 16) | (inv & 0xFFFFu);
+  if (c > w.kth) {
+    w.list = insert_one(w.list, c);
+    w.kth = readlane(w.list, w.km1);
+  }
+}
+
+// Wave-uniform thresholds of the fast filter, from the k-th kept key T.
+struct Filter {
+  bool nonneg;     // T >= +-0: trip when int16(bits) > t16
+  int32_t t16;     // T's magnitude (T >= 0)
+  uint32_t tu;     // T < 0: trip when uint16(bits) < tu (= T's bits); 0x10000 while not full
+  uint32_t ftrip;  // trip when uint16(bits) >= ftrip: -inf / NaN patterns not flagged yet
+};
+
+__device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
+  const uint32_t tkey = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.kth) >> 16;
+  const uint32_t flags = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags);
+  Filter f;
+  f.nonneg = tkey >= 0x8000u;
+  f.t16 = (int32_t)tkey - 0x8000;
+  f.tu = 0x10000u - tkey;
+  f.ftrip = (flags & kNinf) ? ((flags & kNan) ? 0x10000u : 0xFF81u) : 0xFF80u;
+  return f;
+}
+
+__device__ __forceinline__ v2i16 as_i16x2(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
+__device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
+
+// Does any of this lane's N vectors hold an element that may beat the k-th or
+// carries an unflagged -inf / NaN?  (Never a false negative; a false positive
+// only costs the exact path.)
+template <int N>
+__device__ __forceinline__ bool lane_trips(const uint4 (&v)[N], const Filter &f) {
+  v2u16 hi = as_u16x2(v[0].x);
+  if (f.nonneg) {
+    v2i16 a = as_i16x2(v[0].x);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a = __builtin_elementwise_max(a, as_i16x2(dw[q]));
+        hi = __builtin_elementwise_max(hi, as_u16x2(dw[q]));
+      }
+    }
+    const int32_t amax = max((int32_t)a.x, (int32_t)a.y);
+    const uint32_t hmax = max((uint32_t)hi.x, (uint32_t)hi.y);
+    return amax > f.t16 || hmax >= f.ftrip;
+  } else {
+    v2u16 lo = as_u16x2(v[0].x);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo = __builtin_elementwise_min(lo, as_u16x2(dw[q]));
+        hi = __builtin_elementwise_max(hi, as_u16x2(dw[q]));
+      }
+    }
+    const uint32_t lmin = min((uint32_t)lo.x, (uint32_t)lo.y);
+    const uint32_t hmax = max((uint32_t)hi.x, (uint32_t)hi.y);
+    return lmin < f.tu || hmax >= f.ftrip;
+  }
+}
+
+// Exact path for one 16-byte vector per lane when many lanes trip (while the
+// kept set is young): composites of all eight elements, a per-lane sort, then
+// insertion position by position.  Its eight elements sit at columns col0 ..
+// col0 + 7 with inv0 = 0xFFFF - (col0 - wave base).
+__device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t inv0, bool valid) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint32_t c[8];
+  bool nan = false, ninf = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+    const uint32_t key = order_key(b);
+    nan |= (b & 0x7FFFu) > 0x7F80u;
+    ninf |= b == 0xFF80u;
+    c[e] = (valid && key) ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
+  }
+  if (ballot(valid && nan)) w.flags |= kNan;
+  if (ballot(valid && ninf)) w.flags |= kNinf;
+  sort8_desc(c);
+  // each lane's values are descending and the k-th only rises: once no lane
+  // beats it at some position, no later position can
+#pragma unroll 1
+  for (int p = 0; p < 8; ++p) {
+    if (!ballot(c[0] > w.kth)) break;
+    offer(w, c[0]);
+    c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7];
+  }
+}
+
+// Exact path for one 16-byte vector per lane when few lanes trip: a per-element
+// predicate against the filter, then each hit is classified and inserted with
+// wave-uniform (scalar) arithmetic.
+__device__ __forceinline__ void take_vector_sparse(WaveTopK &w, uint4 d, uint32_t inv0, bool valid) {
+  const Filter f = make_filter(w);
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+    const bool beats = f.nonneg ? (int32_t)(int16_t)b > f.t16 : b < f.tu;
+    uint64_t m = ballot(valid && (beats || b >= f.ftrip));
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      take_one(w, readlane(b, l), readlane(inv0, l) - (uint32_t)e);
+    }
+  }
+}
+
+constexpr int kDenseLanes = 16;  // this many tripping lanes pick the dense path
+
+__device__ __forceinline__ void take_vector(WaveTopK &w, uint4 d, uint32_t inv0, bool valid) {
+  const uint4 one[1] = {d};
+  const uint64_t m = ballot(valid && lane_trips<1>(one, make_filter(w)));
+  if (!m) return;
+  if (__popcll(m) >= kDenseLanes) take_vector_dense(w, d, inv0, valid);
+  else take_vector_sparse(w, d, inv0, valid);
+}
+
+// Exact path for columns [lo, hi) one per lane (row edges and tiny spans).
+__device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64_t hi, int64_t base) {
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? (uint32_t)row[col] : 0u;
+    const uint32_t key = order_key(b);
+    if (ballot(valid && (b & 0x7FFFu) > 0x7F80u)) w.flags |= kNan;
+    if (ballot(valid && b == 0xFF80u)) w.flags |= kNinf;
+    const uint32_t c = (valid && key) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
+    offer(w, c);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-family parts
+
+// One chunk of kChunkVecs vectors per lane.  Vector u of this lane is the
+// wave's vector (first + u * 64 + lane); lanes whose vector lies at or past
+// nvec read zeros (the buffer's range check) and are masked out of the exact
+// path.
+__device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
+                                           int64_t col_first, int64_t base) {
+  if (!ballot(lane_trips<kChunkVecs>(v, make_filter(w)))) return;
+  const uint32_t l = (uint32_t)lane_id();
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  static_assert(kChunkVecs == 4, "rotation below");
+  // 0xFFFF - rel of element 0 of this lane's vector (first + l)
+  uint32_t inv0 = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
+  uint32_t vi = first + l;
+#pragma unroll 1
+  for (int u = 0; u < kChunkVecs; ++u) {
+    take_vector(w, x0, inv0, vi < nvec);
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+    inv0 -= (uint32_t)(kWave * kVecElems);
+    vi += (uint32_t)kWave;
+  }
+}
+
+// Loads vectors [first, first + kChunkVecs * 64) of the wave's nvec vectors at
+// vp.  The descriptor is rebuilt per chunk in scalar registers (base advanced,
+// range shrunk), so the per-lane offset stays loop-invariant and the range
+// check zero-fills lanes past the end -- every load is issued unconditionally
+// and the wait counts are the same on every path.
+__device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4 *vp, uint32_t nvec, uint32_t first,
+                                           uint32_t lane_off) {
+  // all wave-uniform; readfirstlane keeps the descriptor in scalar registers
+  first = (uint32_t)__builtin_amdgcn_readfirstlane((int)first);
+  nvec = (uint32_t)__builtin_amdgcn_readfirstlane((int)nvec);
+  const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(nvec - min(first, nvec)));
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vp + first), (short)0, (int)(left * 16u), kBufferWord3);
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(lane_off + (uint32_t)(u * kWave * 16)), 0, 0);
+    dst[u] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
+// Streams nvec 16-byte vectors starting at vp (its first element is column
+// col_first), two chunks in flight.
+__device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t nvec, int64_t col_first,
+                                          int64_t base) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;  // vectors per chunk
+  const uint32_t lane_off = (uint32_t)lane_id() * 16u;
+  uint4 A[kChunkVecs], B[kChunkVecs];
+  load_chunk(A, vp, nvec, 0, lane_off);
+  for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+    load_chunk(B, vp, nvec, first + kStep, lane_off);
+    take_chunk(w, A, first, nvec, col_first, base);
+    if (first + kStep >= nvec) break;
+    load_chunk(A, vp, nvec, first + 2 * kStep, lane_off);
+    take_chunk(w, B, first + kStep, nvec, col_first, base);
+  }
+}
+
+__device__ __forceinline__ uint64_t composite64(uint32_t c32, int64_t base) {
+  if (!c32) return 0;
+  const uint32_t col = (uint32_t)(base + (int64_t)(0xFFFFu - (c32 & 0xFFFFu)));
+  return ((uint64_t)(c32 >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - col);
+}
+
+__device__ __forceinline__ int32_t col_of(uint64_t x) { return (int32_t)(0xFFFFFFFFu - (uint32_t)x); }
+
+// bf16 bits of an entry: the key is invertible except for the shared key of
+// +0 and -0, whose sign is read back from the input.
+__device__ __forceinline__ uint16_t value_bits(uint64_t x, const uint16_t *row) {
+  const uint32_t key = (uint32_t)(x >> 32);
+  if (key > 0x8000u) return (uint16_t)(key - 0x8000u);
+  if (key < 0x8000u) return (uint16_t)(0x8000u | (0x8000u - key));
+  return row[col_of(x)];
+}
+
+// Number of entries of the descending list[0, n) that beat x.
+__device__ __forceinline__ int count_beating(const uint64_t *list, int n, uint64_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
+  __shared__ uint64_t s_list[kWgWaves][kWave];
+  __shared__ int32_t s_count[kWgWaves];
+  __shared__ uint32_t s_flags[kWgWaves];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));  // uniform per wave
+  const int l = lane_id();
+  const uint16_t *row = a.in + r * a.stride;
+
+  // The row's 16-byte grid: vector j covers columns [a0 + 8j, a0 + 8j + 8).
+  const int64_t a0 = (int64_t)((8u - (uint32_t)(((uintptr_t)row >> 1) & 7u)) & 7u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kVecElems : 0;
+  int64_t j0 = 0, j1 = 0, head_lo = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kVecElems * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+  const int64_t base = (wave == 0 && head_hi > head_lo) ? head_lo : a0 + kVecElems * wv0;
+
+  WaveTopK w;
+  w.list = 0;
+  w.kth = 0;
+  w.flags = 0;
+  w.km1 = a.k - 1;
+
+  if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
+  if (wv1 > wv0)
+    take_body(w, reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), a0 + kVecElems * wv0, base);
+  if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns(w, row, tail_lo, tail_hi, base);
+
+  // publish this wave's list
+  const uint64_t valid_mask = ballot(w.list != 0);
+  s_list[wave][l] = composite64(w.list, base);
+  if (l == 0) {
+    const int cnt = __popcll(valid_mask);
+    s_count[wave] = cnt < a.k ? cnt : a.k;
+    s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == kKeyPosInf ? kPinf : 0u);
+  }
+  __syncthreads();
+
+  int total = 0;
+  uint32_t flags = 0;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    total += s_count[o];
+    flags |= s_flags[o];
+  }
+  if (total > a.k) total = a.k;
+
+  const uint64_t x = s_list[wave][l];
+  const bool mine = l < s_count[wave];
+  int rank = l;
+  if (mine) {
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o)
+      if (o != wave) rank += count_beating(s_list[o], s_count[o], x);
+  }
+
+  if (S == 1) {
+    const int64_t ob = r * a.k;
+    if (mine && rank < a.k) {
+      a.out_idx[ob + rank] = col_of(x);
+      a.out_val[ob + rank] = value_bits(x, row);
+    }
+    const int t = threadIdx.x;
+    if (t >= total && t < a.k) {
+      a.out_idx[ob + t] = TK_FILL_IDX;
+      a.out_val[ob + t] = (uint16_t)TK_FILL_VAL;
+    }
+    if (t == 0) {
+      a.out_count[r] = total;
+      a.out_nonfinite[r] = flags;
+    }
+  } else {
+    const int64_t sb = r * S + s;
+    if (mine && rank < a.k) a.span_list[sb * a.k + rank] = x;
+    if (threadIdx.x == 0) {
+      a.span_count[sb] = total;
+      a.span_flags[sb] = flags;
+    }
+  }
+}
+
+// Folds up to kMergeGroup sorted candidate lists of one row into one: pairs
+// are merged round by round in LDS (a tournament); each candidate's place in a
+// pair is its own position plus the number of the partner's entries that beat
+// it.
+__global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
+  __shared__ uint64_t s_buf[2][kMergeGroup * kMaxK];
+  __shared__ int32_t s_cnt[2][kMergeGroup];
+  __shared__ uint32_t s_flags;
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.lists_out;
+  const int g = (int)(blk % a.lists_out);
+  const int first = g * a.group;
+  int n = a.lists_in - first;
+  if (n > a.group) n = a.group;
+  const int k = a.k;
+  const int t = threadIdx.x;
+
+  if (t == 0) s_flags = 0;
+  __syncthreads();
+  const int64_t in_base = r * a.lists_in + first;
+  for (int i = t; i < n * k; i += kMergeThreads) s_buf[0][i] = a.list_in[in_base * k + i];
+  for (int i = t; i < n; i += kMergeThreads) {
+    s_cnt[0][i] = a.count_in[in_base + i];
+    atomicOr(&s_flags, a.flags_in[in_base + i]);
+  }
+  __syncthreads();
+
+  int cur = 0;
+  while (n > 1) {
+    const int nout = (n + 1) >> 1;
+    const uint64_t *src = s_buf[cur];
+    uint64_t *dst = s_buf[cur ^ 1];
+    for (int i = t; i < n * k; i += kMergeThreads) {
+      const int li = i / k;
+      const int p = i - li * k;
+      if (p >= s_cnt[cur][li]) continue;
+      const uint64_t x = src[i];
+      const int partner = li ^ 1;
+      int rank = p;
+      if (partner < n) rank += count_beating(src + partner * k, s_cnt[cur][partner], x);
+      if (rank < k) dst[(li >> 1) * k + rank] = x;
+    }
+    for (int i = t; i < nout; i += kMergeThreads) {
+      int c = s_cnt[cur][2 * i];
+      if (2 * i + 1 < n) c += s_cnt[cur][2 * i + 1];
+      s_cnt[cur ^ 1][i] = c < k ? c : k;
+    }
+    __syncthreads();
+    cur ^= 1;
+    n = nout;
+  }
+
+  const int cnt = s_cnt[cur][0];
+  const uint64_t *res = s_buf[cur];
+  if (a.lists_out == 1) {
+    const uint16_t *row = a.in + r * a.stride;
+    const int64_t ob = r * k;
+    for (int j = t; j < k; j += kMergeThreads) {
+      if (j < cnt) {
+        a.out_idx[ob + j] = col_of(res[j]);
+        a.out_val[ob + j] = value_bits(res[j], row);
+      } else {
+        a.out_idx[ob + j] = TK_FILL_IDX;
+        a.out_val[ob + j] = (uint16_t)TK_FILL_VAL;
+      }
+    }
+    if (t == 0) {
+      a.out_count[r] = cnt;
+      a.out_nonfinite[r] = s_flags;
+    }
+  } else {
+    const int64_t ob = r * a.lists_out + g;
+    for (int j = t; j < cnt; j += kMergeThreads) a.list_out[ob * k + j] = res[j];
+    if (t == 0) {
+      a.count_out[ob] = cnt;
+      a.flags_out[ob] = s_flags;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream) {
+  const int64_t blocks = rows_in_launch * a.spans;
+  hipLaunchKernelGGL(span_scan_kernel, dim3((uint32_t)blocks), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream) {
+  const int64_t blocks = rows_in_launch * a.lists_out;
+  hipLaunchKernelGGL(span_merge_kernel, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tk

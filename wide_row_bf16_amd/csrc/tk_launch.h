@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (tk_api.cpp) and the kernels
+// (tk_kernels.hip).  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace tk {
+
+// One scan workgroup per (row, span).  Rows [row0, row0 + rows_in_launch) of
+// the matrix are covered by rows_in_launch * spans workgroups.  With spans == 1
+// the scan writes the final outputs; otherwise it writes one sorted candidate
+// list per (row, span) into the span arrays for the merge dispatch.
+struct ScanArgs {
+  const uint16_t *in;
+  int64_t row0;
+  int64_t cols;
+  int64_t stride;
+  int32_t k;
+  int32_t spans;
+  int32_t *out_idx;
+  uint16_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+  uint64_t *span_list;  // [rows][spans][k] composite (key << 32 | ~col), descending
+  int32_t *span_count;  // [rows][spans]
+  uint32_t *span_flags; // [rows][spans]
+};
+
+// One merge workgroup per (row, group of up to kMergeGroup input lists).
+// With lists_out == 1 the merge writes the final outputs.
+struct MergeArgs {
+  const uint16_t *in;  // the input matrix: entry values are read back from it
+  int64_t row0;
+  int64_t stride;
+  int32_t k;
+  int32_t lists_in;    // lists per row on input
+  int32_t lists_out;   // lists per row on output = ceil(lists_in / group)
+  int32_t group;       // input lists folded by one workgroup
+  const uint64_t *list_in;
+  const int32_t *count_in;
+  const uint32_t *flags_in;
+  uint64_t *list_out;
+  int32_t *count_out;
+  uint32_t *flags_out;
+  int32_t *out_idx;
+  uint16_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+};
+
+hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
+hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
+
+}  // namespace tk
