@@ -59,7 +59,7 @@ extern "C" {
 
 typedef enum tk_status {
   TK_OK = 0,
-  TK_ERR_NULL = 1,   /* a required pointer is NULL (rows > 0) */
+  TK_ERR_NULL = 1,   /* a required pointer is NULL: with rows > 0 every output, and `in` when cols > 0 */
   TK_ERR_SHAPE = 2,  /* rows < 0, cols < 0, cols > INT32_MAX, row_stride < cols, or sizes overflow */
   TK_ERR_K = 3,      /* k < 1 or k > TK_MAX_K */
   TK_ERR_ALIGN = 4,  /* in/out_val not 2-byte aligned, or out_idx/out_count/out_nonfinite not 4-byte aligned */

@@ -50,6 +50,7 @@ def test_guard_accepts_valid_calls():
     assert v() == OK
     assert v(rows=0, i=None, o=None, val=None, c=None, m=None) == OK  # empty: nothing is touched
     assert v(cols=0, stride=0) == OK
+    assert v(cols=0, stride=0, i=None) == OK  # nothing of the input is read
     assert v(k=64) == OK and v(k=1) == OK
     assert v(k=64, cols=3, stride=3) == OK  # k may exceed cols
     assert v(i=IN + 2, val=VAL + 2) == OK    # 2-byte alignment is enough for bf16 buffers

@@ -1,0 +1,119 @@
+"""Robustness of the HIP path: nothing written outside the outputs, repeat
+runs bit-identical, concurrent streams equal to solo runs (the invariant the
+TensorFold pages check as "concurrent == solo"), and rejected calls leave the
+outputs untouched."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_same, log, need_gpu, to_numpy, upload
+from synth import family_rows, make_config_input
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 0x5A5A
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def canaried_outputs(rows, k, pad=16):
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    bufs = [
+        torch.full((rows * k + 2 * pad,), CANARY, dtype=torch.int32, device="cuda"),
+        torch.full((rows * k + 2 * pad,), CANARY, dtype=torch.int16, device="cuda"),
+        torch.full((rows + 2 * pad,), CANARY, dtype=torch.int32, device="cuda"),
+        torch.full((rows + 2 * pad,), CANARY, dtype=torch.int32, device="cuda"),
+    ]
+    out = tk.TopK(
+        bufs[0][pad:pad + rows * k].view(rows, k),
+        bufs[1][pad:pad + rows * k].view(rows, k).view(torch.bfloat16),
+        bufs[2][pad:pad + rows],
+        bufs[3][pad:pad + rows],
+    )
+    return bufs, out
+
+
+def canaries_intact(bufs, pad=16):
+    for b in bufs:
+        h = b.cpu().numpy()
+        if not (np.all(h[:pad] == CANARY) and np.all(h[-pad:] == CANARY)):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("spans", [0, 1, 7])
+def test_nothing_written_outside_outputs(spans):
+    import wide_row_bf16_amd as tk
+
+    for fam, rows, cols, k in (("mixed_nonfinite", 5, 70001, 20), ("all_nan", 3, 999, 64), ("normal", 1, 4096, 1)):
+        m = family_rows(fam, rows, cols, cols + 5, seed=rows)
+        bufs, out = canaried_outputs(rows, k)
+        log(f"canary {fam} spans={spans}")
+        tk.topk_bf16(upload(m), k, cols=cols, spans=spans if spans <= cols else 0, out=out)
+        got = to_numpy(out)
+        assert canaries_intact(bufs)
+        assert_same(got, oracle.topk_bf16(m, cols, k), f"canary {fam}")
+
+
+def test_repeat_runs_bit_identical():
+    import wide_row_bf16_amd as tk
+
+    m = make_config_input("c4")
+    x = upload(m)
+    first = to_numpy(tk.topk_bf16(x, 16, cols=151936))
+    for _ in range(5):
+        again = to_numpy(tk.topk_bf16(x, 16, cols=151936))
+        assert_same(again, first, "repeat")
+
+
+def test_concurrent_streams_equal_solo():
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    ms = [family_rows(f, 16, 151936, 152064, seed=i) for i, f in enumerate(("logit", "normal", "levels64", "mixed_nonfinite"))]
+    xs = [upload(m) for m in ms]
+    solo = [to_numpy(tk.topk_bf16(x, 16, cols=151936)) for x in xs]
+    streams = [torch.cuda.Stream() for _ in xs]
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        for x, s in zip(xs, streams):
+            with torch.cuda.stream(s):
+                outs.append(tk.topk_bf16(x, 16, cols=151936, spans=4))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert_same(to_numpy(o), solo[i % 4], f"stream {i % 4}")
+
+
+def test_rejected_calls_write_nothing():
+    import wide_row_bf16_amd as tk
+
+    m = family_rows("normal", 4, 1000, 1000, seed=3)
+    x = upload(m)
+    bufs, out = canaried_outputs(4, 8)
+    for kw in (dict(spans=2000), dict(spans=-1)):
+        with pytest.raises(tk.TkError) as e:
+            tk.topk_bf16(x, 8, out=out, **kw)
+        assert e.value.status == 7
+    with pytest.raises(tk.TkError) as e:
+        tk.topk_bf16(x, 65, out=out)
+    assert e.value.status == 3
+    for b in bufs:
+        assert np.all(b.cpu().numpy() == CANARY)
+
+
+def test_many_rows():
+    for rows, cols, k in ((70000, 64, 8), (5000, 1500, 64), (300, 30000, 5)):
+        m = family_rows("uniform_bits", rows, cols, cols, seed=rows)
+        log(f"many rows {rows}x{cols} k={k}")
+        from gpu_util import check_case
+
+        check_case(m, cols, k, what=f"{rows}x{cols}")

@@ -38,7 +38,7 @@ tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const voi
   if (rows < 0 || cols < 0 || cols > INT32_MAX || stride < cols) return TK_ERR_SHAPE;
   if (k < 1 || k > kMaxK) return TK_ERR_K;
   if (rows == 0) return TK_OK;
-  if (!in || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;
+  if ((cols > 0 && !in) || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;
   const int64_t big = std::numeric_limits<int64_t>::max() / 8;
   if (!mul_ok(rows - 1, stride, big) || (rows - 1) * stride > big - cols) return TK_ERR_SHAPE;
   if (!mul_ok(rows, k, big)) return TK_ERR_SHAPE;
