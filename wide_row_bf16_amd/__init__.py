@@ -126,6 +126,13 @@ def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr
     return int(lib.tk_topk_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
 
 
+def _current_stream_handle(torch, dev: int) -> int:
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(dev))
+    return int(torch.cuda.current_stream(dev).cuda_stream)
+
+
 def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, out: TopK | None = None, stream=None) -> TopK:
     """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
 
@@ -156,10 +163,15 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, out: TopK |
             torch.empty((rows,), dtype=torch.int32, device=x.device),
             torch.empty((rows,), dtype=torch.int32, device=x.device),
         )
-    st = stream if stream is not None else torch.cuda.current_stream(x.device)
-    with torch.cuda.device(x.device):
-        status = topk_bf16_raw(rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(),
-                               out.count.data_ptr(), out.nonfinite.data_ptr(), st.cuda_stream, spans)
+    dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
+    args = (rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
+            out.nonfinite.data_ptr(), handle, spans)
+    if dev == torch.cuda.current_device():
+        status = topk_bf16_raw(*args)
+    else:
+        with torch.cuda.device(dev):
+            status = topk_bf16_raw(*args)
     if status != TK_OK:
         raise TkError(status, "tk_topk_bf16")
     return out

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <limits>
+#include <mutex>
 
 #include "tk_config.h"
 #include "tk_launch.h"
@@ -108,6 +109,56 @@ void keep_pool(int dev) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Span lists need device scratch.  Each (device, stream) keeps one buffer
+// between calls so that a call makes no allocation once warm; a buffer grows
+// stream-ordered (hipFreeAsync of the old one, hipMallocAsync of the new one,
+// both on that stream, so work already queued there still sees the old one).
+// Calls on one stream are ordered by the stream itself; the mutex orders the
+// host side from lookup to the last launch.  Requests above kCacheMaxBytes,
+// or beyond kCacheStreams distinct streams, allocate and free per call.
+constexpr size_t kCacheMaxBytes = size_t(64) << 20;
+constexpr int kCacheStreams = 64;
+
+struct ScratchSlot {
+  int dev;
+  hipStream_t stream;
+  void *ptr;
+  size_t cap;
+};
+
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kCacheStreams];
+int g_scratch_used = 0;
+
+// With g_scratch_mu held: a cached buffer of at least `bytes` for (dev,
+// stream), or nullptr when the request is not cached (the caller allocates).
+void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st) {
+  *st = TK_OK;
+  if (bytes > kCacheMaxBytes) return nullptr;
+  ScratchSlot *slot = nullptr;
+  for (int i = 0; i < g_scratch_used; ++i)
+    if (g_scratch[i].dev == dev && g_scratch[i].stream == stream) slot = &g_scratch[i];
+  if (!slot) {
+    if (g_scratch_used == kCacheStreams) return nullptr;
+    slot = &g_scratch[g_scratch_used++];
+    *slot = ScratchSlot{dev, stream, nullptr, 0};
+  }
+  if (slot->cap < bytes) {
+    size_t cap = slot->cap * 2 > bytes ? slot->cap * 2 : bytes;
+    if (cap > kCacheMaxBytes) cap = kCacheMaxBytes < bytes ? bytes : kCacheMaxBytes;
+    if (slot->ptr && hipFreeAsync(slot->ptr, stream) != hipSuccess) *st = TK_ERR_DEVICE;
+    slot->ptr = nullptr;
+    slot->cap = 0;
+    if (*st == TK_OK && hipMallocAsync(&slot->ptr, cap, stream) != hipSuccess) {
+      slot->ptr = nullptr;
+      *st = TK_ERR_DEVICE;
+    }
+    if (*st != TK_OK) return nullptr;
+    slot->cap = cap;
+  }
+  return slot->ptr;
+}
+
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
               const tk_options *opt) {
@@ -166,8 +217,12 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
     total = align256(total + nlists * sizeof(uint32_t));
   }
   keep_pool(dev);
-  void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  tk_status sst = TK_OK;
+  void *scratch = cached_scratch(dev, stream, total, &sst);
+  if (sst != TK_OK) return sst;
+  const bool owned = scratch == nullptr;
+  if (owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
   char *base = (char *)scratch;
 
   tk_status result = TK_OK;
@@ -213,7 +268,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
       }
     }
   }
-  if (hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  if (owned && hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
   return result;
 }
 

@@ -61,77 +61,145 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
+// Lane exchanges.  Partners at xor distances 1, 2, 3 (quad_perm), 7
+// (row_half_mirror), 15 (row_mirror) and 8 (row_ror:8) are single DPP moves;
+// distance 4 takes one of two row rotations; distances 16 and 32 use the
+// gfx950 permlane swaps.  Which rotation, and which half of a swap, holds
+// lane ^ d is found once per wave from lane ids (Xchg), so nothing here depends
+// on a rotate or swap direction convention.
+struct Xchg {
+  bool ror4;  // row_ror:4 delivers lane ^ 4 to this lane (else row_ror:12 does)
+  bool sw16;  // the first result of permlane16_swap(v, v) holds lane ^ 16
+  bool sw32;  // the first result of permlane32_swap(v, v) holds lane ^ 32
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ Xchg make_xchg() {
+  const uint32_t l = (uint32_t)lane_id();
+  Xchg x;
+  x.ror4 = dpp<0x124>(l) == (l ^ 4u);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  x.sw16 = s16[0] == (l ^ 16u);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+  x.sw32 = s32[0] == (l ^ 32u);
+  return x;
+}
+
 // v from lane (lane ^ MASK).
 template <int MASK>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  static_assert(MASK > 0 && MASK < 64, "lane mask");
+__device__ __forceinline__ uint32_t partner(uint32_t v, const Xchg &x) {
   if constexpr (MASK == 1) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    return dpp<0xB1>(v);  // quad_perm [1,0,3,2]
   } else if constexpr (MASK == 2) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (MASK < 32) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (MASK << 10));  // xor within 32 lanes
+    return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (MASK == 3) {
+    return dpp<0x1B>(v);  // quad_perm [3,2,1,0]
+  } else if constexpr (MASK == 7) {
+    return dpp<0x141>(v);  // row_half_mirror
+  } else if constexpr (MASK == 15) {
+    return dpp<0x140>(v);  // row_mirror
+  } else if constexpr (MASK == 8) {
+    return dpp<0x128>(v);  // row_ror:8
+  } else if constexpr (MASK == 4) {
+    const uint32_t a = dpp<0x124>(v), b = dpp<0x12C>(v);  // row_ror:4, row_ror:12
+    return x.ror4 ? a : b;
+  } else if constexpr (MASK == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return x.sw16 ? s[0] : s[1];
   } else if constexpr (MASK == 32) {
-    return (uint32_t)__shfl_xor((int)v, 32);
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return x.sw32 ? s[0] : s[1];
+  } else if constexpr (MASK == 31) {
+    return partner<16>(partner<15>(v, x), x);
   } else {
-    return xor_lane<32>(xor_lane<MASK - 32>(v));
+    static_assert(MASK == 63, "unsupported lane distance");
+    return partner<32>(partner<31>(v, x), x);
   }
 }
 
-// One compare-exchange stage of a bitonic network over the 64 lanes.  Blocks
-// of SIZE lanes alternate direction so that the final SIZE == 64 stage sorts
-// descending.
-template <int SIZE, int STRIDE>
-__device__ __forceinline__ uint32_t bitonic_stage(uint32_t x) {
-  const uint32_t y = xor_lane<STRIDE>(x);
-  const int l = lane_id();
-  const bool ascending_block = (SIZE < 64) && (l & SIZE);
-  const bool lower = !(l & STRIDE);
-  return (lower != ascending_block) ? max(x, y) : min(x, y);
+// One compare-exchange stage over the 64 lanes: the lane whose LOW bit is
+// clear keeps the larger value.
+template <int MASK, int LOW>
+__device__ __forceinline__ uint32_t cx_stage(uint32_t v, const Xchg &x) {
+  const uint32_t y = partner<MASK>(v, x);
+  return (lane_id() & LOW) ? min(v, y) : max(v, y);
 }
 
-__device__ __forceinline__ uint32_t sort64_desc(uint32_t x) {
-  x = bitonic_stage<2, 1>(x);
-  x = bitonic_stage<4, 2>(x);
-  x = bitonic_stage<4, 1>(x);
-  x = bitonic_stage<8, 4>(x);
-  x = bitonic_stage<8, 2>(x);
-  x = bitonic_stage<8, 1>(x);
-  x = bitonic_stage<16, 8>(x);
-  x = bitonic_stage<16, 4>(x);
-  x = bitonic_stage<16, 2>(x);
-  x = bitonic_stage<16, 1>(x);
-  x = bitonic_stage<32, 16>(x);
-  x = bitonic_stage<32, 8>(x);
-  x = bitonic_stage<32, 4>(x);
-  x = bitonic_stage<32, 2>(x);
-  x = bitonic_stage<32, 1>(x);
-  x = bitonic_stage<64, 32>(x);
-  x = bitonic_stage<64, 16>(x);
-  x = bitonic_stage<64, 8>(x);
-  x = bitonic_stage<64, 4>(x);
-  x = bitonic_stage<64, 2>(x);
-  x = bitonic_stage<64, 1>(x);
-  return x;
+// Descending bitonic sort across the 64 lanes, in the form where every block
+// of `size` lanes starts with a mirrored compare (lane ^ (size - 1)) followed
+// by half-cleaners (lane ^ size/4, ..., lane ^ 1).
+__device__ __forceinline__ uint32_t sort64_desc(uint32_t v, const Xchg &x) {
+  v = cx_stage<1, 1>(v, x);
+  v = cx_stage<3, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  v = cx_stage<7, 4>(v, x);
+  v = cx_stage<2, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  v = cx_stage<15, 8>(v, x);
+  v = cx_stage<4, 4>(v, x);
+  v = cx_stage<2, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  v = cx_stage<31, 16>(v, x);
+  v = cx_stage<8, 8>(v, x);
+  v = cx_stage<4, 4>(v, x);
+  v = cx_stage<2, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  v = cx_stage<63, 32>(v, x);
+  v = cx_stage<16, 16>(v, x);
+  v = cx_stage<8, 8>(v, x);
+  v = cx_stage<4, 4>(v, x);
+  v = cx_stage<2, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  return v;
 }
 
 // Sorts a bitonic sequence over the 64 lanes into descending order.
-__device__ __forceinline__ uint32_t bitonic_merge64_desc(uint32_t x) {
-  x = bitonic_stage<64, 32>(x);
-  x = bitonic_stage<64, 16>(x);
-  x = bitonic_stage<64, 8>(x);
-  x = bitonic_stage<64, 4>(x);
-  x = bitonic_stage<64, 2>(x);
-  x = bitonic_stage<64, 1>(x);
-  return x;
+__device__ __forceinline__ uint32_t bitonic_merge64_desc(uint32_t v, const Xchg &x) {
+  v = cx_stage<32, 32>(v, x);
+  v = cx_stage<16, 16>(v, x);
+  v = cx_stage<8, 8>(v, x);
+  v = cx_stage<4, 4>(v, x);
+  v = cx_stage<2, 2>(v, x);
+  v = cx_stage<1, 1>(v, x);
+  return v;
 }
 
-// The 64 best of (list, x): sort x, reverse it against the descending list,
+// The 64 best of (list, v): sort v, reverse it against the descending list,
 // keep the lane-wise maximum (a bitonic sequence holding the 64 best of the
 // union) and sort that.
-__device__ __forceinline__ uint32_t merge_batch(uint32_t list, uint32_t x) {
-  x = xor_lane<63>(sort64_desc(x));
-  return bitonic_merge64_desc(max(list, x));
+__device__ __forceinline__ uint32_t merge_batch(uint32_t list, uint32_t v, const Xchg &x) {
+  v = partner<63>(sort64_desc(v, x), x);
+  return bitonic_merge64_desc(max(list, v), x);
+}
+
+// 64-bit versions for the cross-span merge (composite key << 32 | ~column).
+template <int MASK>
+__device__ __forceinline__ uint64_t partner64(uint64_t v, const Xchg &x) {
+  const uint32_t lo = partner<MASK>((uint32_t)v, x), hi = partner<MASK>((uint32_t)(v >> 32), x);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int MASK, int LOW>
+__device__ __forceinline__ uint64_t cx_stage64(uint64_t v, const Xchg &x) {
+  const uint64_t y = partner64<MASK>(v, x);
+  return (lane_id() & LOW) ? (v < y ? v : y) : (v > y ? v : y);
+}
+
+// The 64 best of two descending lists held one entry per lane.
+__device__ __forceinline__ uint64_t merge_sorted64(uint64_t a, uint64_t b, const Xchg &x) {
+  b = partner64<63>(b, x);
+  uint64_t v = a > b ? a : b;
+  v = cx_stage64<32, 32>(v, x);
+  v = cx_stage64<16, 16>(v, x);
+  v = cx_stage64<8, 8>(v, x);
+  v = cx_stage64<4, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  return v;
 }
 
 // Inserts one composite c into the descending list: lanes before its place
@@ -168,8 +236,13 @@ __device__ __forceinline__ uint32_t order_key(uint32_t b) {
 struct WaveTopK {
   uint32_t list;   // lane i: i-th best composite so far, 0 = empty
   uint32_t kth;    // wave-uniform copy of list[k - 1]
+  uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of other waves
   uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
   int km1;         // k - 1
+  int qm1;         // ceil(k / 4) - 1
+  int wave;        // this wave's index in the workgroup
+  uint32_t *tau;   // LDS: published k-th keys of the workgroup's waves
+  Xchg x;
 };
 
 // Adds candidates c (one per lane, 0 = none) whose composite beats the k-th.
@@ -177,7 +250,7 @@ __device__ __forceinline__ void offer(WaveTopK &w, uint32_t c) {
   uint64_t m = ballot(c > w.kth);
   if (!m) return;
   if (__popcll(m) >= kBatchInsert) {
-    w.list = merge_batch(w.list, c > w.kth ? c : 0u);
+    w.list = merge_batch(w.list, c > w.kth ? c : 0u, w.x);
   } else {
     do {
       const int l = __builtin_ctzll(m);
@@ -193,30 +266,63 @@ __device__ __forceinline__ void offer(WaveTopK &w, uint32_t c) {
 }
 
 // One element whose bits b (wave-uniform) may beat the k-th or carry an
-// unflagged -inf / NaN; inv = 0xFFFF - (column - wave base).
+// unflagged -inf / NaN; inv = 0xFFFF - (column - wave base).  NaN gets key 0,
+// which never exceeds ext, so it is flagged and never kept.
 __device__ __forceinline__ void take_one(WaveTopK &w, uint32_t b, uint32_t inv) {
-  if ((b & 0x7FFFu) > 0x7F80u) {
-    w.flags |= kNan;
-    return;
-  }
-  if (b == 0xFF80u) w.flags |= kNinf;
-  const uint32_t c = (order_key(b) << 16) | (inv & 0xFFFFu);
-  if (c > w.kth) {
+  const uint32_t key = order_key(b);
+  w.flags |= key == 0 ? kNan : (b == 0xFF80u ? kNinf : 0u);
+  const uint32_t c = (key << 16) | (inv & 0xFFFFu);
+  if (key > w.ext && c > w.kth) {
     w.list = insert_one(w.list, c);
     w.kth = readlane(w.list, w.km1);
   }
 }
 
-// Wave-uniform thresholds of the fast filter, from the k-th kept key T.
+// Threshold sharing between the waves of a workgroup.  Each wave publishes
+// two keys of its kept list: tau = its k-th entry and q = its ceil(k/4)-th
+// entry (0 while it holds fewer).  Two bounds follow, each meaning "k kept
+// entries of the workgroup beat every key below it":
+//  - one wave's tau: a wave to the left (lower columns) also beats keys equal
+//    to tau, since on equal keys the lower column wins; a wave to the right
+//    beats only keys < tau;
+//  - the smallest q of all four waves: each holds ceil(k/4) entries >= it, so
+//    k entries beat every key below it (equal keys may lie either side).
+// For evenly spread data the second is about the k-th key of the union.
+// Published values only rise, so a stale read is still a valid bound.
+__device__ __forceinline__ uint32_t shared_bound(const uint32_t *s_tau, int wave) {
+  uint32_t ext = 0, qmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    const uint32_t t = __hip_atomic_load(&s_tau[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t q = __hip_atomic_load(&s_tau[kWgWaves + o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t b = o < wave ? t : (t > 0 ? t - 1 : 0u);
+    if (o != wave) ext = max(ext, b);
+    qmin = min(qmin, q);
+  }
+  if (qmin > 0) ext = max(ext, qmin - 1);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ext);
+}
+
+__device__ __forceinline__ void publish(uint32_t *s_tau, int wave, const WaveTopK &w) {
+  const uint32_t q = readlane(w.list, w.qm1) >> 16;
+  if (lane_id() == 0) {
+    __hip_atomic_store(&s_tau[wave], w.kth >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&s_tau[kWgWaves + wave], q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Wave-uniform thresholds of the fast filter from T = max(k-th kept key, ext):
+// an element may matter only if its key exceeds T.
 struct Filter {
   bool nonneg;     // T >= +-0: trip when int16(bits) > t16
   int32_t t16;     // T's magnitude (T >= 0)
-  uint32_t tu;     // T < 0: trip when uint16(bits) < tu (= T's bits); 0x10000 while not full
+  uint32_t tu;     // T < 0: trip when uint16(bits) < tu (= T's bits); 0x10000 while nothing bounds it
   uint32_t ftrip;  // trip when uint16(bits) >= ftrip: -inf / NaN patterns not flagged yet
 };
 
 __device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
-  const uint32_t tkey = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.kth) >> 16;
+  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.kth) >> 16;
+  const uint32_t tkey = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
   const uint32_t flags = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags);
   Filter f;
   f.nonneg = tkey >= 0x8000u;
@@ -229,41 +335,34 @@ __device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
 __device__ __forceinline__ v2i16 as_i16x2(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 
-// Does any of this lane's N vectors hold an element that may beat the k-th or
-// carries an unflagged -inf / NaN?  (Never a false negative; a false positive
-// only costs the exact path.)
+// Bit u set: this lane's vector u holds an element whose key may exceed T or
+// that carries an unflagged -inf / NaN.  (Never a false negative; a false
+// positive only costs the exact path.)
 template <int N>
-__device__ __forceinline__ bool lane_trips(const uint4 (&v)[N], const Filter &f) {
-  v2u16 hi = as_u16x2(v[0].x);
+__device__ __forceinline__ uint32_t lane_trip_bits(const uint4 (&v)[N], const Filter &f) {
+  uint32_t bits = 0;
   if (f.nonneg) {
-    v2i16 a = as_i16x2(v[0].x);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a = __builtin_elementwise_max(a, as_i16x2(dw[q]));
-        hi = __builtin_elementwise_max(hi, as_u16x2(dw[q]));
-      }
+      const v2i16 a = __builtin_elementwise_max(__builtin_elementwise_max(as_i16x2(v[u].x), as_i16x2(v[u].y)),
+                                                __builtin_elementwise_max(as_i16x2(v[u].z), as_i16x2(v[u].w)));
+      const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
+                                                __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
+      const bool t = max((int32_t)a.x, (int32_t)a.y) > f.t16 || max((uint32_t)h.x, (uint32_t)h.y) >= f.ftrip;
+      bits |= (uint32_t)t << u;
     }
-    const int32_t amax = max((int32_t)a.x, (int32_t)a.y);
-    const uint32_t hmax = max((uint32_t)hi.x, (uint32_t)hi.y);
-    return amax > f.t16 || hmax >= f.ftrip;
   } else {
-    v2u16 lo = as_u16x2(v[0].x);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lo = __builtin_elementwise_min(lo, as_u16x2(dw[q]));
-        hi = __builtin_elementwise_max(hi, as_u16x2(dw[q]));
-      }
+      const v2u16 lo = __builtin_elementwise_min(__builtin_elementwise_min(as_u16x2(v[u].x), as_u16x2(v[u].y)),
+                                                 __builtin_elementwise_min(as_u16x2(v[u].z), as_u16x2(v[u].w)));
+      const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
+                                                __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
+      const bool t = min((uint32_t)lo.x, (uint32_t)lo.y) < f.tu || max((uint32_t)h.x, (uint32_t)h.y) >= f.ftrip;
+      bits |= (uint32_t)t << u;
     }
-    const uint32_t lmin = min((uint32_t)lo.x, (uint32_t)lo.y);
-    const uint32_t hmax = max((uint32_t)hi.x, (uint32_t)hi.y);
-    return lmin < f.tu || hmax >= f.ftrip;
   }
+  return bits;
 }
 
 // Exact path for one 16-byte vector per lane when many lanes trip (while the
@@ -280,7 +379,7 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
     const uint32_t key = order_key(b);
     nan |= (b & 0x7FFFu) > 0x7F80u;
     ninf |= b == 0xFF80u;
-    c[e] = (valid && key) ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
+    c[e] = (valid && key > w.ext) ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
   }
   if (ballot(valid && nan)) w.flags |= kNan;
   if (ballot(valid && ninf)) w.flags |= kNinf;
@@ -295,34 +394,30 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
   }
 }
 
-// Exact path for one 16-byte vector per lane when few lanes trip: a per-element
-// predicate against the filter, then each hit is classified and inserted with
-// wave-uniform (scalar) arithmetic.
-__device__ __forceinline__ void take_vector_sparse(WaveTopK &w, uint4 d, uint32_t inv0, bool valid) {
-  const Filter f = make_filter(w);
+// Exact path for one 16-byte vector when few lanes trip: a per-element
+// predicate over all lanes against the vector's starting thresholds (a
+// conservative pre-test: they only rise), then each hit is classified and
+// inserted with wave-uniform arithmetic.  NONNEG selects the filter form
+// (int16 compare for T >= 0, uint16 compare for T < 0).
+template <bool NONNEG>
+__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv0, bool valid, const Filter &f) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-    const bool beats = f.nonneg ? (int32_t)(int16_t)b > f.t16 : b < f.tu;
+    const uint32_t word = dw[e >> 1];
+    const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
+    const bool beats = NONNEG ? (int32_t)(int16_t)b > f.t16 : b < f.tu;
     uint64_t m = ballot(valid && (beats || b >= f.ftrip));
     while (m) {
       const int l = __builtin_ctzll(m);
       m &= m - 1;
-      take_one(w, readlane(b, l), readlane(inv0, l) - (uint32_t)e);
+      const uint32_t wl = readlane(word, l);
+      take_one(w, (e & 1) ? wl >> 16 : wl & 0xFFFFu, readlane(inv0, l) - (uint32_t)e);
     }
   }
 }
 
 constexpr int kDenseLanes = 16;  // this many tripping lanes pick the dense path
-
-__device__ __forceinline__ void take_vector(WaveTopK &w, uint4 d, uint32_t inv0, bool valid) {
-  const uint4 one[1] = {d};
-  const uint64_t m = ballot(valid && lane_trips<1>(one, make_filter(w)));
-  if (!m) return;
-  if (__popcll(m) >= kDenseLanes) take_vector_dense(w, d, inv0, valid);
-  else take_vector_sparse(w, d, inv0, valid);
-}
 
 // Exact path for columns [lo, hi) one per lane (row edges and tiny spans).
 __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64_t hi, int64_t base) {
@@ -333,7 +428,7 @@ __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64
     const uint32_t key = order_key(b);
     if (ballot(valid && (b & 0x7FFFu) > 0x7F80u)) w.flags |= kNan;
     if (ballot(valid && b == 0xFF80u)) w.flags |= kNinf;
-    const uint32_t c = (valid && key) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
+    const uint32_t c = (valid && key > w.ext) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
     offer(w, c);
   }
 }
@@ -344,10 +439,14 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-fa
 // One chunk of kChunkVecs vectors per lane.  Vector u of this lane is the
 // wave's vector (first + u * 64 + lane); lanes whose vector lies at or past
 // nvec read zeros (the buffer's range check) and are masked out of the exact
-// path.
+// path.  Trip bits are taken once against the thresholds at the chunk start:
+// the thresholds only rise while the chunk is processed, so a lane that did
+// not trip then cannot hold anything that matters later.
 __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                            int64_t col_first, int64_t base) {
-  if (!ballot(lane_trips<kChunkVecs>(v, make_filter(w)))) return;
+  w.ext = shared_bound(w.tau, w.wave);
+  uint32_t bits = lane_trip_bits<kChunkVecs>(v, make_filter(w));
+  if (!ballot(bits != 0)) return;
   const uint32_t l = (uint32_t)lane_id();
   uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
   static_assert(kChunkVecs == 4, "rotation below");
@@ -356,13 +455,28 @@ __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkV
   uint32_t vi = first + l;
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
-    take_vector(w, x0, inv0, vi < nvec);
+    const bool valid = vi < nvec;
+    const uint64_t m = ballot(valid && (bits & 1u));
+    if (m) {
+      if (__popcll(m) >= kDenseLanes) {
+        take_vector_dense(w, x0, inv0, valid);
+        // the young set just grew a lot: share it and take the others' news
+        publish(w.tau, w.wave, w);
+        w.ext = shared_bound(w.tau, w.wave);
+      } else {
+        const Filter f = make_filter(w);
+        if (f.nonneg) take_lanes_ballot<true>(w, x0, inv0, valid, f);
+        else take_lanes_ballot<false>(w, x0, inv0, valid, f);
+      }
+    }
+    bits >>= 1;
     x0 = x1;
     x1 = x2;
     x2 = x3;
     inv0 -= (uint32_t)(kWave * kVecElems);
     vi += (uint32_t)kWave;
   }
+  publish(w.tau, w.wave, w);
 }
 
 // Loads vectors [first, first + kChunkVecs * 64) of the wave's nvec vectors at
@@ -434,6 +548,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   __shared__ uint64_t s_list[kWgWaves][kWave];
   __shared__ int32_t s_count[kWgWaves];
   __shared__ uint32_t s_flags[kWgWaves];
+  __shared__ uint32_t s_tau[2 * kWgWaves];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -463,11 +578,18 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
   const int64_t base = (wave == 0 && head_hi > head_lo) ? head_lo : a0 + kVecElems * wv0;
 
+  if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
+  __syncthreads();
   WaveTopK w;
   w.list = 0;
   w.kth = 0;
+  w.ext = 0;
   w.flags = 0;
   w.km1 = a.k - 1;
+  w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
+  w.wave = wave;
+  w.tau = s_tau;
+  w.x = make_xchg();
 
   if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
   if (wv1 > wv0)
@@ -527,14 +649,16 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   }
 }
 
-// Folds up to kMergeGroup sorted candidate lists of one row into one: pairs
-// are merged round by round in LDS (a tournament); each candidate's place in a
-// pair is its own position plus the number of the partner's entries that beat
-// it.
+// Folds up to kMergeGroup sorted candidate lists of one row into one.  Each
+// wave of the workgroup loads lists straight into registers (lane j holds
+// entry j) and folds them pairwise with bitonic merges of the 64-bit
+// composites -- the same (score desc, column asc) order as the scan; the four
+// wave results then meet in LDS and wave 0 folds them.
 __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
-  __shared__ uint64_t s_buf[2][kMergeGroup * kMaxK];
-  __shared__ int32_t s_cnt[2][kMergeGroup];
-  __shared__ uint32_t s_flags;
+  __shared__ uint64_t s_acc[kMergeThreads / kWave][kWave];
+  __shared__ int32_t s_cnt[kMergeThreads / kWave];
+  __shared__ uint32_t s_flags[kMergeThreads / kWave];
+  constexpr int kWaves = kMergeThreads / kWave;
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.lists_out;
@@ -543,67 +667,58 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
   int n = a.lists_in - first;
   if (n > a.group) n = a.group;
   const int k = a.k;
-  const int t = threadIdx.x;
-
-  if (t == 0) s_flags = 0;
-  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const Xchg x = make_xchg();
   const int64_t in_base = r * a.lists_in + first;
-  for (int i = t; i < n * k; i += kMergeThreads) s_buf[0][i] = a.list_in[in_base * k + i];
-  for (int i = t; i < n; i += kMergeThreads) {
-    s_cnt[0][i] = a.count_in[in_base + i];
-    atomicOr(&s_flags, a.flags_in[in_base + i]);
+
+  uint64_t acc = 0;
+  int cnt = 0;
+  uint32_t flags = 0;
+  for (int li = wave; li < n; li += kWaves) {
+    const int c = a.count_in[in_base + li];
+    flags |= a.flags_in[in_base + li];
+    const uint64_t v = l < c ? a.list_in[(in_base + li) * k + l] : 0;
+    acc = li == wave ? v : merge_sorted64(acc, v, x);
+    cnt += c;
+  }
+  s_acc[wave][l] = acc;
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_flags[wave] = flags;
   }
   __syncthreads();
-
-  int cur = 0;
-  while (n > 1) {
-    const int nout = (n + 1) >> 1;
-    const uint64_t *src = s_buf[cur];
-    uint64_t *dst = s_buf[cur ^ 1];
-    for (int i = t; i < n * k; i += kMergeThreads) {
-      const int li = i / k;
-      const int p = i - li * k;
-      if (p >= s_cnt[cur][li]) continue;
-      const uint64_t x = src[i];
-      const int partner = li ^ 1;
-      int rank = p;
-      if (partner < n) rank += count_beating(src + partner * k, s_cnt[cur][partner], x);
-      if (rank < k) dst[(li >> 1) * k + rank] = x;
-    }
-    for (int i = t; i < nout; i += kMergeThreads) {
-      int c = s_cnt[cur][2 * i];
-      if (2 * i + 1 < n) c += s_cnt[cur][2 * i + 1];
-      s_cnt[cur ^ 1][i] = c < k ? c : k;
-    }
-    __syncthreads();
-    cur ^= 1;
-    n = nout;
+  if (wave != 0) return;
+#pragma unroll
+  for (int o = 1; o < kWaves; ++o) {
+    acc = merge_sorted64(acc, s_acc[o][l], x);
+    cnt += s_cnt[o];
+    flags |= s_flags[o];
   }
+  if (cnt > k) cnt = k;
 
-  const int cnt = s_cnt[cur][0];
-  const uint64_t *res = s_buf[cur];
   if (a.lists_out == 1) {
     const uint16_t *row = a.in + r * a.stride;
     const int64_t ob = r * k;
-    for (int j = t; j < k; j += kMergeThreads) {
-      if (j < cnt) {
-        a.out_idx[ob + j] = col_of(res[j]);
-        a.out_val[ob + j] = value_bits(res[j], row);
+    if (l < k) {
+      if (l < cnt) {
+        a.out_idx[ob + l] = col_of(acc);
+        a.out_val[ob + l] = value_bits(acc, row);
       } else {
-        a.out_idx[ob + j] = TK_FILL_IDX;
-        a.out_val[ob + j] = (uint16_t)TK_FILL_VAL;
+        a.out_idx[ob + l] = TK_FILL_IDX;
+        a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;
       }
     }
-    if (t == 0) {
+    if (l == 0) {
       a.out_count[r] = cnt;
-      a.out_nonfinite[r] = s_flags;
+      a.out_nonfinite[r] = flags;
     }
   } else {
     const int64_t ob = r * a.lists_out + g;
-    for (int j = t; j < cnt; j += kMergeThreads) a.list_out[ob * k + j] = res[j];
-    if (t == 0) {
+    if (l < cnt) a.list_out[ob * k + l] = acc;
+    if (l == 0) {
       a.count_out[ob] = cnt;
-      a.flags_out[ob] = s_flags;
+      a.flags_out[ob] = flags;
     }
   }
 }
