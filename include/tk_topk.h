@@ -88,10 +88,14 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
  *          candidate lists a second dispatch merges.  Rejected with
  *          TK_ERR_OPTION when a span would exceed the library's span limit
  *          (tk_max_span_cols()) or n > cols (for cols > 0).
+ *   exact  0 = automatic; 1 = never take the speculative floor (wide spans
+ *          otherwise skip elements below a floor estimated from a sample and
+ *          verify it afterwards, scanning again when it does not hold).
  */
 typedef struct tk_options {
   int32_t spans;
-  int32_t reserved[7]; /* must be zero */
+  int32_t exact;
+  int32_t reserved[6]; /* must be zero */
 } tk_options;
 
 tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,

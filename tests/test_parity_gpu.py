@@ -134,3 +134,42 @@ def test_configs_full_size(name):
     for spans in (0, 1):
         log(f"config {name} spans={spans}")
         assert_same(gpu_topk(m, cfg.cols, cfg.k, spans=spans, x=x), want, f"{name} spans={spans}")
+
+
+@pytest.mark.parametrize("family", ["normal", "logit", "levels64", "mixed_nonfinite", "uniform_bits", "ascending",
+                                    "descending", "zeros_straddle", "all_equal", "neginf_one_finite"])
+def test_speculative_floor_and_exact_mode(family):
+    """Wide single-span rows take the speculative floor; the exact mode and the
+    floor must give the oracle's bytes alike."""
+    cols = 248320
+    m = family_rows(family, 3, cols, cols, seed=77)
+    x = upload(m)
+    for k in (1, 9, 64):
+        want = oracle.topk_bf16(m, cols, k)
+        for exact in (False, True):
+            log(f"speculative family={family} k={k} exact={exact}")
+            got = gpu_topk(m, cols, k, spans=1, x=x) if not exact else _exact(x, cols, k)
+            assert_same(got, want, f"{family} k={k} exact={exact}")
+
+
+def _exact(x, cols, k):
+    import wide_row_bf16_amd as tk
+    from gpu_util import to_numpy
+
+    return to_numpy(tk.topk_bf16(x, k, cols=cols, spans=1, exact=True))
+
+
+def test_speculation_falls_back_when_floor_is_too_high():
+    """Three huge values at the start of each wave's share put the floor so
+    high that only 12 elements reach it: k = 64 must scan again, k = 8 must
+    verify.  (Each wave of a single-span 151936-column row starts at a
+    multiple of 37984 columns for 16-byte aligned rows.)"""
+    cols = 151936
+    m = family_rows("normal", 4, cols, cols, seed=5)
+    for w in range(4):
+        for j in range(3):
+            m[:, 37984 * w + j] = 0x42C8  # 100.0
+    x = upload(m)
+    for k in (8, 12, 13, 64):
+        log(f"fallback k={k}")
+        assert_same(gpu_topk(m, cols, k, spans=1, x=x), oracle.topk_bf16(m, cols, k), f"fallback k={k}")

@@ -45,7 +45,7 @@ class TkError(RuntimeError):
 
 
 class TkOptions(ctypes.Structure):
-    _fields_ = [("spans", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("spans", ctypes.c_int32), ("exact", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 class TopK(NamedTuple):
@@ -116,11 +116,12 @@ def validate(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mas
     return int(load().tk_validate_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr))
 
 
-def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream=0, spans=0) -> int:
+def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream=0, spans=0,
+                  exact=0) -> int:
     """Calls the C ABI on raw device pointers; returns the status code."""
     lib = load()
-    if spans:
-        opt = TkOptions(spans=spans)
+    if spans or exact:
+        opt = TkOptions(spans=spans, exact=exact)
         return int(lib.tk_topk_bf16_ex(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
                                        stream, ctypes.byref(opt)))
     return int(lib.tk_topk_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
@@ -133,11 +134,13 @@ def _current_stream_handle(torch, dev: int) -> int:
     return int(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, out: TopK | None = None, stream=None) -> TopK:
+def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool = False, out: TopK | None = None,
+              stream=None) -> TopK:
     """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
 
     ``cols`` limits the scan to the first ``cols`` columns (default: all);
     ``spans`` forces the row split (0 = automatic, 1 = one workgroup per row);
+    ``exact`` turns off the speculative floor (the result is the same);
     ``out`` reuses preallocated outputs; ``stream`` is a torch.cuda.Stream
     (default: the current stream).
     """
@@ -166,7 +169,7 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, out: TopK |
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
     args = (rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
-            out.nonfinite.data_ptr(), handle, spans)
+            out.nonfinite.data_ptr(), handle, spans, int(exact))
     if dev == torch.cuda.current_device():
         status = topk_bf16_raw(*args)
     else:

@@ -164,10 +164,12 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
               const tk_options *opt) {
   tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
   if (st != TK_OK) return st;
-  int32_t forced = 0;
+  int32_t forced = 0, exact = 0;
   if (opt) {
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < 6; ++i)
       if (opt->reserved[i] != 0) return TK_ERR_OPTION;
+    if (opt->exact != 0 && opt->exact != 1) return TK_ERR_OPTION;
+    exact = opt->exact;
     forced = opt->spans;
     if (forced < 0 || forced > kMaxSpans) return TK_ERR_OPTION;
     if (forced > 1 && cols > 0 && forced > cols) return TK_ERR_OPTION;
@@ -186,6 +188,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   sa.stride = stride;
   sa.k = k;
   sa.spans = spans;
+  sa.exact = exact;
   sa.out_idx = out_idx;
   sa.out_val = out_val;
   sa.out_count = out_count;

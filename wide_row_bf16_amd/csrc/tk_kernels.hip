@@ -237,6 +237,7 @@ struct WaveTopK {
   uint32_t list;   // lane i: i-th best composite so far, 0 = empty
   uint32_t kth;    // wave-uniform copy of list[k - 1]
   uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of other waves
+  uint32_t floor;  // wave-uniform speculative floor: only keys > floor are kept (0 = none)
   uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
   int km1;         // k - 1
   int qm1;         // ceil(k / 4) - 1
@@ -245,21 +246,16 @@ struct WaveTopK {
   Xchg x;
 };
 
-// Adds candidates c (one per lane, 0 = none) whose composite beats the k-th.
-__device__ __forceinline__ void offer(WaveTopK &w, uint32_t c) {
-  uint64_t m = ballot(c > w.kth);
-  if (!m) return;
+// Adds the candidates c of lanes m (their composites beat the k-th) to the
+// list: one bitonic batch when many, else one insertion each.
+__device__ __forceinline__ void offer(WaveTopK &w, uint32_t c, uint64_t m) {
   if (__popcll(m) >= kBatchInsert) {
     w.list = merge_batch(w.list, c > w.kth ? c : 0u, w.x);
   } else {
     do {
       const int l = __builtin_ctzll(m);
       m &= m - 1;
-      const uint32_t one = readlane(c, l);
-      if (one > w.kth) {
-        w.list = insert_one(w.list, one);
-        w.kth = readlane(w.list, w.km1);
-      }
+      w.list = insert_one(w.list, readlane(c, l));  // stale k-th: see take_one
     } while (m);
   }
   w.kth = readlane(w.list, w.km1);
@@ -267,15 +263,15 @@ __device__ __forceinline__ void offer(WaveTopK &w, uint32_t c) {
 
 // One element whose bits b (wave-uniform) may beat the k-th or carry an
 // unflagged -inf / NaN; inv = 0xFFFF - (column - wave base).  NaN gets key 0,
-// which never exceeds ext, so it is flagged and never kept.
+// which never exceeds ext, so it is flagged and never kept.  The k-th copy is
+// not refreshed here: testing later hits of the same batch against a stale
+// (lower) k-th only lets extra candidates through, and inserting one that no
+// longer qualifies changes list slots >= k only.
 __device__ __forceinline__ void take_one(WaveTopK &w, uint32_t b, uint32_t inv) {
   const uint32_t key = order_key(b);
   w.flags |= key == 0 ? kNan : (b == 0xFF80u ? kNinf : 0u);
   const uint32_t c = (key << 16) | (inv & 0xFFFFu);
-  if (key > w.ext && c > w.kth) {
-    w.list = insert_one(w.list, c);
-    w.kth = readlane(w.list, w.km1);
-  }
+  if (key > w.ext && c > w.kth) w.list = insert_one(w.list, c);
 }
 
 // Threshold sharing between the waves of a workgroup.  Each wave publishes
@@ -388,33 +384,41 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
   // beats it at some position, no later position can
 #pragma unroll 1
   for (int p = 0; p < 8; ++p) {
-    if (!ballot(c[0] > w.kth)) break;
-    offer(w, c[0]);
+    const uint64_t m = ballot(c[0] > w.kth);
+    if (!m) break;
+    offer(w, c[0], m);
     c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7];
   }
 }
 
-// Exact path for one 16-byte vector when few lanes trip: a per-element
-// predicate over all lanes against the vector's starting thresholds (a
-// conservative pre-test: they only rise), then each hit is classified and
-// inserted with wave-uniform arithmetic.  NONNEG selects the filter form
-// (int16 compare for T >= 0, uint16 compare for T < 0).
+// Exact path for one 16-byte vector when few lanes trip: the eight
+// per-element predicates over all lanes are evaluated back to back against
+// the vector's starting thresholds (a conservative pre-test: they only rise),
+// then the hit masks are walked with wave-uniform arithmetic.  NONNEG selects
+// the filter form (int16 compare for T >= 0, uint16 compare for T < 0).
+// inv_l0 is 0xFFFF - rel of element 0 of lane 0's vector; lane l's vector
+// starts 8 l columns later.
 template <bool NONNEG>
-__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv0, bool valid, const Filter &f) {
+__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv_l0, bool valid, const Filter &f) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint64_t m[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
     const bool beats = NONNEG ? (int32_t)(int16_t)b > f.t16 : b < f.tu;
-    uint64_t m = ballot(valid && (beats || b >= f.ftrip));
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t wl = readlane(word, l);
-      take_one(w, (e & 1) ? wl >> 16 : wl & 0xFFFFu, readlane(inv0, l) - (uint32_t)e);
+    m[e] = ballot(valid && (beats || b >= f.ftrip));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    while (m[e]) {
+      const int l = __builtin_ctzll(m[e]);
+      m[e] &= m[e] - 1;
+      const uint32_t wl = readlane(dw[e >> 1], l);
+      take_one(w, (e & 1) ? wl >> 16 : wl & 0xFFFFu, inv_l0 - (uint32_t)(kVecElems * l + e));
     }
   }
+  w.kth = readlane(w.list, w.km1);
 }
 
 constexpr int kDenseLanes = 16;  // this many tripping lanes pick the dense path
@@ -429,7 +433,8 @@ __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64
     if (ballot(valid && (b & 0x7FFFu) > 0x7F80u)) w.flags |= kNan;
     if (ballot(valid && b == 0xFF80u)) w.flags |= kNinf;
     const uint32_t c = (valid && key > w.ext) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
-    offer(w, c);
+    const uint64_t m = ballot(c > w.kth);
+    if (m) offer(w, c, m);
   }
 }
 
@@ -444,11 +449,11 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-fa
 // not trip then cannot hold anything that matters later.
 __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                            int64_t col_first, int64_t base) {
-  w.ext = shared_bound(w.tau, w.wave);
+  w.ext = max(shared_bound(w.tau, w.wave), w.floor);
   uint32_t bits = lane_trip_bits<kChunkVecs>(v, make_filter(w));
   if (!ballot(bits != 0)) return;
   const uint32_t l = (uint32_t)lane_id();
-  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // rotated once per vector below
   static_assert(kChunkVecs == 4, "rotation below");
   // 0xFFFF - rel of element 0 of this lane's vector (first + l)
   uint32_t inv0 = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
@@ -458,15 +463,17 @@ __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkV
     const bool valid = vi < nvec;
     const uint64_t m = ballot(valid && (bits & 1u));
     if (m) {
+      const uint4 d = x0;
       if (__popcll(m) >= kDenseLanes) {
-        take_vector_dense(w, x0, inv0, valid);
+        take_vector_dense(w, d, inv0, valid);
         // the young set just grew a lot: share it and take the others' news
         publish(w.tau, w.wave, w);
-        w.ext = shared_bound(w.tau, w.wave);
+        w.ext = max(shared_bound(w.tau, w.wave), w.floor);
       } else {
         const Filter f = make_filter(w);
-        if (f.nonneg) take_lanes_ballot<true>(w, x0, inv0, valid, f);
-        else take_lanes_ballot<false>(w, x0, inv0, valid, f);
+        const uint32_t inv_l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(inv0 + (uint32_t)kVecElems * l));
+        if (f.nonneg) take_lanes_ballot<true>(w, d, inv_l0, valid, f);
+        else take_lanes_ballot<false>(w, d, inv_l0, valid, f);
       }
     }
     bits >>= 1;
@@ -497,6 +504,39 @@ __device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(lane_off + (uint32_t)(u * kWave * 16)), 0, 0);
     dst[u] = make_uint4(x.x, x.y, x.z, x.w);
   }
+}
+
+// The second-largest order key among this wave's first chunk (vectors
+// [0, kChunkVecs * 64) of the nvec at vp; NaN counts as key 0).  Used to
+// pick a speculative floor; see span_scan_kernel.
+__device__ __forceinline__ uint32_t first_chunk_second_key(const uint4 *vp, uint32_t nvec, const Xchg &x) {
+  uint4 v[kChunkVecs];
+  load_chunk(v, vp, nvec, 0, (uint32_t)lane_id() * 16u);
+  uint32_t m1 = 0, m2 = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t key = order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+      m2 = max(m2, min(m1, key));
+      m1 = max(m1, key);
+    }
+  }
+  // lanes past nvec read zeros, i.e. +0 (key 0x8000); they are excluded by
+  // the caller's requirement that the first chunk is full
+  auto fold = [&](uint32_t o1, uint32_t o2) {
+    const uint32_t n2 = max(min(m1, o1), max(m2, o2));
+    m1 = max(m1, o1);
+    m2 = n2;
+  };
+  fold(partner<1>(m1, x), partner<1>(m2, x));
+  fold(partner<2>(m1, x), partner<2>(m2, x));
+  fold(partner<4>(m1, x), partner<4>(m2, x));
+  fold(partner<8>(m1, x), partner<8>(m2, x));
+  fold(partner<16>(m1, x), partner<16>(m2, x));
+  fold(partner<32>(m1, x), partner<32>(m2, x));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)m2);
 }
 
 // Streams nvec 16-byte vectors starting at vp (its first element is column
@@ -549,6 +589,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   __shared__ int32_t s_count[kWgWaves];
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
+  __shared__ uint32_t s_t0[kWgWaves];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -578,40 +619,70 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
   const int64_t base = (wave == 0 && head_hi > head_lo) ? head_lo : a0 + kVecElems * wv0;
 
-  if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
-  __syncthreads();
-  WaveTopK w;
-  w.list = 0;
-  w.kth = 0;
-  w.ext = 0;
-  w.flags = 0;
-  w.km1 = a.k - 1;
-  w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
-  w.wave = wave;
-  w.tau = s_tau;
-  w.x = make_xchg();
-
-  if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
-  if (wv1 > wv0)
-    take_body(w, reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), a0 + kVecElems * wv0, base);
-  if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns(w, row, tail_lo, tail_hi, base);
-
-  // publish this wave's list
-  const uint64_t valid_mask = ballot(w.list != 0);
-  s_list[wave][l] = composite64(w.list, base);
-  if (l == 0) {
-    const int cnt = __popcll(valid_mask);
-    s_count[wave] = cnt < a.k ? cnt : a.k;
-    s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == kKeyPosInf ? kPinf : 0u);
+  // Speculative floor.  When every wave's share spans at least kSpecChunks
+  // chunks, each wave takes the second-largest key of its first chunk and the
+  // workgroup keeps only keys >= T0, the smallest of those four: at least 8
+  // elements of the span reach T0, typically about 8 * (span / sample) of
+  // them, so the young lists never need filling from scratch.  The result is
+  // verified: if the lists end with k entries (all >= T0), every dropped
+  // element is beaten by k kept ones and the answer is exact; otherwise the
+  // span is scanned again without a floor.
+  uint32_t floor = 0;
+  const bool speculate =
+      !a.exact && a.k <= kSpecMaxK && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
+  if (speculate) {
+    const uint32_t t = first_chunk_second_key(reinterpret_cast<const uint4 *>(row + a0) + wv0,
+                                              (uint32_t)(wv1 - wv0), make_xchg());
+    if (l == 0) s_t0[wave] = t;
+    __syncthreads();
+    uint32_t t0 = s_t0[0];
+#pragma unroll
+    for (int o = 1; o < kWgWaves; ++o) t0 = min(t0, s_t0[o]);
+    floor = t0 > 0 ? t0 - 1 : 0;
   }
-  __syncthreads();
 
   int total = 0;
   uint32_t flags = 0;
+  for (;;) {
+    if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
+    __syncthreads();
+    WaveTopK w;
+    w.list = 0;
+    w.kth = 0;
+    w.ext = floor;
+    w.floor = floor;
+    w.flags = 0;
+    w.km1 = a.k - 1;
+    w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
+    w.wave = wave;
+    w.tau = s_tau;
+    w.x = make_xchg();
+
+    if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
+    if (wv1 > wv0)
+      take_body(w, reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), a0 + kVecElems * wv0, base);
+    if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns(w, row, tail_lo, tail_hi, base);
+
+    // publish this wave's list
+    const uint64_t valid_mask = ballot(w.list != 0);
+    s_list[wave][l] = composite64(w.list, base);
+    if (l == 0) {
+      const int cnt = __popcll(valid_mask);
+      s_count[wave] = cnt < a.k ? cnt : a.k;
+      s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == kKeyPosInf ? kPinf : 0u);
+    }
+    __syncthreads();
+
+    total = 0;
+    flags = 0;
 #pragma unroll
-  for (int o = 0; o < kWgWaves; ++o) {
-    total += s_count[o];
-    flags |= s_flags[o];
+    for (int o = 0; o < kWgWaves; ++o) {
+      total += s_count[o];
+      flags |= s_flags[o];
+    }
+    if (floor == 0 || total >= a.k) break;  // exact, or the speculation verified
+    floor = 0;                              // too few entries reach T0: scan again without it
+    __syncthreads();                        // every wave has read the counts above
   }
   if (total > a.k) total = a.k;
 
@@ -649,16 +720,18 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   }
 }
 
-// Folds up to kMergeGroup sorted candidate lists of one row into one.  Each
-// wave of the workgroup loads lists straight into registers (lane j holds
-// entry j) and folds them pairwise with bitonic merges of the 64-bit
-// composites -- the same (score desc, column asc) order as the scan; the four
-// wave results then meet in LDS and wave 0 folds them.
+// Folds up to kMergeGroup sorted candidate lists of one row into one.  All
+// threads first stage the group's lists in LDS (every load in flight at
+// once), then each wave folds its share pairwise in registers (lane j holds
+// entry j) with bitonic merges of the 64-bit composites -- the same (score
+// desc, column asc) order as the scan -- and wave 0 folds the four results.
 __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
-  __shared__ uint64_t s_acc[kMergeThreads / kWave][kWave];
-  __shared__ int32_t s_cnt[kMergeThreads / kWave];
-  __shared__ uint32_t s_flags[kMergeThreads / kWave];
   constexpr int kWaves = kMergeThreads / kWave;
+  __shared__ uint64_t s_lists[kMergeGroup * kMaxK];
+  __shared__ int32_t s_count[kMergeGroup];
+  __shared__ uint64_t s_acc[kWaves][kWave];
+  __shared__ int32_t s_cnt[kWaves];
+  __shared__ uint32_t s_flags;
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.lists_out;
@@ -667,35 +740,40 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
   int n = a.lists_in - first;
   if (n > a.group) n = a.group;
   const int k = a.k;
+  const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const Xchg x = make_xchg();
   const int64_t in_base = r * a.lists_in + first;
 
+  if (t == 0) s_flags = 0;
+  __syncthreads();
+  for (int i = t; i < n * k; i += kMergeThreads) s_lists[i] = a.list_in[in_base * k + i];
+  for (int i = t; i < n; i += kMergeThreads) {
+    s_count[i] = a.count_in[in_base + i];
+    atomicOr(&s_flags, a.flags_in[in_base + i]);
+  }
+  __syncthreads();
+
   uint64_t acc = 0;
   int cnt = 0;
-  uint32_t flags = 0;
   for (int li = wave; li < n; li += kWaves) {
-    const int c = a.count_in[in_base + li];
-    flags |= a.flags_in[in_base + li];
-    const uint64_t v = l < c ? a.list_in[(in_base + li) * k + l] : 0;
+    const int c = s_count[li];
+    const uint64_t v = l < c ? s_lists[li * k + l] : 0;
     acc = li == wave ? v : merge_sorted64(acc, v, x);
     cnt += c;
   }
   s_acc[wave][l] = acc;
-  if (l == 0) {
-    s_cnt[wave] = cnt;
-    s_flags[wave] = flags;
-  }
+  if (l == 0) s_cnt[wave] = cnt;
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int o = 1; o < kWaves; ++o) {
     acc = merge_sorted64(acc, s_acc[o][l], x);
     cnt += s_cnt[o];
-    flags |= s_flags[o];
   }
   if (cnt > k) cnt = k;
+  const uint32_t flags = s_flags;
 
   if (a.lists_out == 1) {
     const uint16_t *row = a.in + r * a.stride;

@@ -18,6 +18,7 @@ struct ScanArgs {
   int64_t stride;
   int32_t k;
   int32_t spans;
+  int32_t exact;        // 1: never use a speculative floor
   int32_t *out_idx;
   uint16_t *out_val;
   int32_t *out_count;
