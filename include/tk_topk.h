@@ -3,12 +3,12 @@
  *
  * The operation (TensorFold PR #713 "the drafter's attention and top-k use
  * more of the GPU", change 3 and its Exactness table): for every row of a
- * rows x cols matrix of bf16 logits, return the k best entries in
- * "(score, lower token) order" -- score descending, and among equal scores the
- * lower column index first -- together with the row's entry count and a
- * non-finite mask.  Results must be byte-equal across every way the work is
- * split (the page compares its span path with a single-group control) and to
- * a CPU oracle, over ties, both zeros, NaN, infinities and padded strides.
+ * rows x cols matrix of bf16 logits, return the k best entries -- score
+ * descending, and among equal scores the lower column (token) index first --
+ * together with the row's entry count and a non-finite mask.  Results must be
+ * identical byte for byte across every way the work is split (the page
+ * compares its span path with a single-group control) and to a CPU oracle,
+ * over ties, both zeros, NaN, infinities and padded strides.
  *
  * Value policy (plain readings where the page is silent):
  *   NaN   -- any sign or payload; never an entry; sets TK_NONFINITE_NAN.

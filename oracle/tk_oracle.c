@@ -7,8 +7,8 @@
  *
  * What is computed (TensorFold PR #713 "the drafter's attention and top-k use
  * more of the GPU", change 3 and the Exactness table):
- *   - each row's top-k entries in "(score, lower token) order": score
- *     descending, and among equal scores the lower column index first;
+ *   - each row's top-k entries ordered by score, highest first, with ties
+ *     between equal scores going to the lower column (token) index;
  *   - per row an entry count and a non-finite mask;
  *   - the cases that must be exact: ties, both zeros, NaN and infinities, and
  *     padded row strides.

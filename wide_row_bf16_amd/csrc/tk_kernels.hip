@@ -1,11 +1,11 @@
 // Exact row-wise bf16 top-k kernels for CDNA4 (gfx950).
 //
 // What is computed (TensorFold PR #713 "the drafter's attention and top-k use
-// more of the GPU", change 3): each row's k best entries in "(score, lower
-// token) order".  Wide rows may be split into spans whose candidate lists a
-// second dispatch merges "with the same tournament and the same (score, lower
-// token) order"; the result must not depend on the split (Exactness table of
-// the same page).
+// more of the GPU", change 3): each row's k best entries, highest score first,
+// equal scores ordered by the lower column (token) index.  Wide rows may be
+// split into spans whose candidate lists a second dispatch merges under that
+// same order; the result must not depend on the split (Exactness table of the
+// same page).
 //
 // Order key.  A bf16 pattern b with magnitude m = b & 0x7FFF maps to the
 // 16-bit key 0x8000 + m (sign clear) or 0x8000 - m (sign set).  The key is
