@@ -57,6 +57,13 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Lane masks straight from a compare (one v_cmp writing a scalar register
+// pair; no detour of the per-lane result through a vector register).
+__device__ __forceinline__ uint64_t lanes_sgt(int32_t a, int32_t b) { return __builtin_amdgcn_sicmp(a, b, 38); }
+__device__ __forceinline__ uint64_t lanes_ugt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 34); }
+__device__ __forceinline__ uint64_t lanes_uge(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 35); }
+__device__ __forceinline__ uint64_t lanes_ult(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36); }
+
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
@@ -331,12 +338,11 @@ __device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
 __device__ __forceinline__ v2i16 as_i16x2(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 
-// Bit u set: this lane's vector u holds an element whose key may exceed T or
-// that carries an unflagged -inf / NaN.  (Never a false negative; a false
+// trip[u]: the lanes whose vector u holds an element whose key may exceed T
+// or that carries an unflagged -inf / NaN.  (Never a false negative; a false
 // positive only costs the exact path.)
 template <int N>
-__device__ __forceinline__ uint32_t lane_trip_bits(const uint4 (&v)[N], const Filter &f) {
-  uint32_t bits = 0;
+__device__ __forceinline__ void lane_trips(const uint4 (&v)[N], const Filter &f, uint64_t (&trip)[N]) {
   if (f.nonneg) {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
@@ -344,8 +350,8 @@ __device__ __forceinline__ uint32_t lane_trip_bits(const uint4 (&v)[N], const Fi
                                                 __builtin_elementwise_max(as_i16x2(v[u].z), as_i16x2(v[u].w)));
       const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
                                                 __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
-      const bool t = max((int32_t)a.x, (int32_t)a.y) > f.t16 || max((uint32_t)h.x, (uint32_t)h.y) >= f.ftrip;
-      bits |= (uint32_t)t << u;
+      trip[u] = lanes_sgt(max((int32_t)a.x, (int32_t)a.y), f.t16) |
+                lanes_uge(max((uint32_t)h.x, (uint32_t)h.y), f.ftrip);
     }
   } else {
 #pragma unroll
@@ -354,11 +360,10 @@ __device__ __forceinline__ uint32_t lane_trip_bits(const uint4 (&v)[N], const Fi
                                                  __builtin_elementwise_min(as_u16x2(v[u].z), as_u16x2(v[u].w)));
       const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
                                                 __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
-      const bool t = min((uint32_t)lo.x, (uint32_t)lo.y) < f.tu || max((uint32_t)h.x, (uint32_t)h.y) >= f.ftrip;
-      bits |= (uint32_t)t << u;
+      trip[u] = lanes_ult(min((uint32_t)lo.x, (uint32_t)lo.y), f.tu) |
+                lanes_uge(max((uint32_t)h.x, (uint32_t)h.y), f.ftrip);
     }
   }
-  return bits;
 }
 
 // Exact path for one 16-byte vector per lane when many lanes trip (while the
@@ -384,7 +389,7 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
   // beats it at some position, no later position can
 #pragma unroll 1
   for (int p = 0; p < 8; ++p) {
-    const uint64_t m = ballot(c[0] > w.kth);
+    const uint64_t m = lanes_ugt(c[0], w.kth);
     if (!m) break;
     offer(w, c[0], m);
     c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7];
@@ -399,15 +404,16 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
 // inv_l0 is 0xFFFF - rel of element 0 of lane 0's vector; lane l's vector
 // starts 8 l columns later.
 template <bool NONNEG>
-__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv_l0, bool valid, const Filter &f) {
+__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv_l0, uint64_t valid,
+                                                  const Filter &f) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
   uint64_t m[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
-    const bool beats = NONNEG ? (int32_t)(int16_t)b > f.t16 : b < f.tu;
-    m[e] = ballot(valid && (beats || b >= f.ftrip));
+    const uint64_t beats = NONNEG ? lanes_sgt((int32_t)(int16_t)b, f.t16) : lanes_ult(b, f.tu);
+    m[e] = (beats | lanes_uge(b, f.ftrip)) & valid;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -433,7 +439,7 @@ __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64
     if (ballot(valid && (b & 0x7FFFu) > 0x7F80u)) w.flags |= kNan;
     if (ballot(valid && b == 0xFF80u)) w.flags |= kNinf;
     const uint32_t c = (valid && key > w.ext) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
-    const uint64_t m = ballot(c > w.kth);
+    const uint64_t m = lanes_ugt(c, w.kth);
     if (m) offer(w, c, m);
   }
 }
@@ -450,22 +456,23 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-fa
 __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                            int64_t col_first, int64_t base) {
   w.ext = max(shared_bound(w.tau, w.wave), w.floor);
-  uint32_t bits = lane_trip_bits<kChunkVecs>(v, make_filter(w));
-  if (!ballot(bits != 0)) return;
+  uint64_t trip[kChunkVecs];
+  lane_trips<kChunkVecs>(v, make_filter(w), trip);
+  static_assert(kChunkVecs == 4, "rotation below");
+  if (!(trip[0] | trip[1] | trip[2] | trip[3])) return;
   const uint32_t l = (uint32_t)lane_id();
   uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // rotated once per vector below
-  static_assert(kChunkVecs == 4, "rotation below");
   // 0xFFFF - rel of element 0 of this lane's vector (first + l)
   uint32_t inv0 = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
   uint32_t vi = first + l;
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
-    const bool valid = vi < nvec;
-    const uint64_t m = ballot(valid && (bits & 1u));
+    const uint64_t valid = lanes_ult(vi, nvec);
+    const uint64_t m = trip[0] & valid;
     if (m) {
       const uint4 d = x0;
       if (__popcll(m) >= kDenseLanes) {
-        take_vector_dense(w, d, inv0, valid);
+        take_vector_dense(w, d, inv0, vi < nvec);
         // the young set just grew a lot: share it and take the others' news
         publish(w.tau, w.wave, w);
         w.ext = max(shared_bound(w.tau, w.wave), w.floor);
@@ -476,7 +483,9 @@ __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkV
         else take_lanes_ballot<false>(w, d, inv_l0, valid, f);
       }
     }
-    bits >>= 1;
+    trip[0] = trip[1];
+    trip[1] = trip[2];
+    trip[2] = trip[3];
     x0 = x1;
     x1 = x2;
     x2 = x3;
