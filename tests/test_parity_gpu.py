@@ -160,15 +160,16 @@ def _exact(x, cols, k):
 
 
 def test_speculation_falls_back_when_floor_is_too_high():
-    """Three huge values at the start of each wave's share put the floor so
-    high that only 12 elements reach it: k = 64 must scan again, k = 8 must
-    verify.  (Each wave of a single-span 151936-column row starts at a
-    multiple of 37984 columns for 16-byte aligned rows.)"""
+    """Three huge values in the first vectors of three lanes of each wave put
+    the floor's sample keys so high that only 12 elements reach it: k = 13 and
+    k = 64 must scan again, k = 8 and k = 12 must verify.  (Each wave of a
+    single-span 151936-column row starts at a multiple of 37984 columns for
+    16-byte aligned rows, and lane i's first vector starts 8 i columns in.)"""
     cols = 151936
     m = family_rows("normal", 4, cols, cols, seed=5)
     for w in range(4):
-        for j in range(3):
-            m[:, 37984 * w + j] = 0x42C8  # 100.0
+        for i in range(3):
+            m[:, 37984 * w + 8 * i] = 0x42C8  # 100.0
     x = upload(m)
     for k in (8, 12, 13, 64):
         log(f"fallback k={k}")

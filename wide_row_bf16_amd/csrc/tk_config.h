@@ -23,8 +23,7 @@ constexpr int kMergeGroup = 64;                // span lists one merge workgroup
 constexpr int kMergeThreads = 256;
 constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
-constexpr int kSpecMaxK = 48;                  // above this k the floor admits about as many as the
-                                               // exact bounds do, spread over more chunks (measured)
+constexpr int kSpecMargin = 3;                 // the floor's sample rank targets this many times k keys
 
 static_assert(kMaxK == (int)TK_MAX_K, "public and internal max k differ");
 static_assert(kMaxK <= kWave, "a wave holds one kept entry per lane");

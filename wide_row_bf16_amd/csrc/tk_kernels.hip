@@ -515,37 +515,23 @@ __device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4
   }
 }
 
-// The second-largest order key among this wave's first chunk (vectors
-// [0, kChunkVecs * 64) of the nvec at vp; NaN counts as key 0).  Used to
-// pick a speculative floor; see span_scan_kernel.
-__device__ __forceinline__ uint32_t first_chunk_second_key(const uint4 *vp, uint32_t nvec, const Xchg &x) {
+// The j-th largest of the 64 per-lane maximum order keys of this wave's first
+// chunk (vectors [0, kChunkVecs * 64) of the nvec at vp; NaN counts as key 0),
+// j <= 64.  At least j elements of the chunk reach it, and for j much smaller
+// than 64 it is about the j-th largest key of the chunk.  Used to pick a
+// speculative floor; see span_scan_kernel.
+__device__ __forceinline__ uint32_t first_chunk_key(const uint4 *vp, uint32_t nvec, int j, const Xchg &x) {
   uint4 v[kChunkVecs];
   load_chunk(v, vp, nvec, 0, (uint32_t)lane_id() * 16u);
-  uint32_t m1 = 0, m2 = 0;
+  uint32_t m = 0;
 #pragma unroll
   for (int u = 0; u < kChunkVecs; ++u) {
     const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t key = order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-      m2 = max(m2, min(m1, key));
-      m1 = max(m1, key);
-    }
+    for (int e = 0; e < 8; ++e) m = max(m, order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
   }
-  // lanes past nvec read zeros, i.e. +0 (key 0x8000); they are excluded by
-  // the caller's requirement that the first chunk is full
-  auto fold = [&](uint32_t o1, uint32_t o2) {
-    const uint32_t n2 = max(min(m1, o1), max(m2, o2));
-    m1 = max(m1, o1);
-    m2 = n2;
-  };
-  fold(partner<1>(m1, x), partner<1>(m2, x));
-  fold(partner<2>(m1, x), partner<2>(m2, x));
-  fold(partner<4>(m1, x), partner<4>(m2, x));
-  fold(partner<8>(m1, x), partner<8>(m2, x));
-  fold(partner<16>(m1, x), partner<16>(m2, x));
-  fold(partner<32>(m1, x), partner<32>(m2, x));
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)m2);
+  // the caller only asks when the first chunk is full
+  return readlane(sort64_desc(m, x), j - 1);
 }
 
 // Streams nvec 16-byte vectors starting at vp (its first element is column
@@ -629,19 +615,23 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   const int64_t base = (wave == 0 && head_hi > head_lo) ? head_lo : a0 + kVecElems * wv0;
 
   // Speculative floor.  When every wave's share spans at least kSpecChunks
-  // chunks, each wave takes the second-largest key of its first chunk and the
-  // workgroup keeps only keys >= T0, the smallest of those four: at least 8
-  // elements of the span reach T0, typically about 8 * (span / sample) of
-  // them, so the young lists never need filling from scratch.  The result is
-  // verified: if the lists end with k entries (all >= T0), every dropped
-  // element is beaten by k kept ones and the answer is exact; otherwise the
-  // span is scanned again without a floor.
+  // chunks, each wave takes a high key T_w from a sample (its first chunk)
+  // and the workgroup keeps only keys >= T0 = min T_w.  T_w is the sample's
+  // j-th largest (about), with j chosen so that about kSpecMargin * k keys of
+  // the span are expected to reach it.  The result is verified: if the lists
+  // end with k entries (all >= T0), every dropped element is beaten by k kept
+  // ones and the answer is exact; otherwise the span is scanned again without
+  // a floor, which the margin makes rare.
   uint32_t floor = 0;
-  const bool speculate =
-      !a.exact && a.k <= kSpecMaxK && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
+  const bool speculate = !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
   if (speculate) {
-    const uint32_t t = first_chunk_second_key(reinterpret_cast<const uint4 *>(row + a0) + wv0,
-                                              (uint32_t)(wv1 - wv0), make_xchg());
+    // expected keys of the span >= the sample's j-th largest: j * 8 n / sample
+    constexpr int64_t kSample = (int64_t)kChunkVecs * kWave * kVecElems;
+    const int64_t want = (int64_t)kSpecMargin * a.k * kSample;
+    int j = (int)((want + kVecElems * n - 1) / (kVecElems * n));
+    j = j < 2 ? 2 : (j > kWave ? kWave : j);
+    const uint32_t t = first_chunk_key(reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), j,
+                                       make_xchg());
     if (l == 0) s_t0[wave] = t;
     __syncthreads();
     uint32_t t0 = s_t0[0];
