@@ -160,17 +160,18 @@ def _exact(x, cols, k):
 
 
 def test_speculation_falls_back_when_floor_is_too_high():
-    """Three huge values in the first vectors of three lanes of each wave put
-    the floor's sample keys so high that only 12 elements reach it: k = 13 and
-    k = 64 must scan again, k = 8 and k = 12 must verify.  (Each wave of a
-    single-span 151936-column row starts at a multiple of 37984 columns for
-    16-byte aligned rows, and lane i's first vector starts 8 i columns in.)"""
+    """Large values in the first vectors of 15 lanes of each wave (60 in all)
+    fill the top of the floor's sample, so the speculative floor lands on them
+    whenever its rank is at most 60: k = 61 and k = 64 must scan again, k = 8
+    and k = 60 verify.  (Each wave of a single-span 151936-column row starts at
+    a multiple of 37984 columns for 16-byte aligned rows, and lane i's first
+    vector starts 8 i columns in.)"""
     cols = 151936
     m = family_rows("normal", 4, cols, cols, seed=5)
     for w in range(4):
-        for i in range(3):
+        for i in range(15):
             m[:, 37984 * w + 8 * i] = 0x42C8  # 100.0
     x = upload(m)
-    for k in (8, 12, 13, 64):
+    for k in (8, 60, 61, 64):
         log(f"fallback k={k}")
         assert_same(gpu_topk(m, cols, k, spans=1, x=x), oracle.topk_bf16(m, cols, k), f"fallback k={k}")

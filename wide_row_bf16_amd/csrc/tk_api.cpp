@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cmath>
 #include <limits>
 #include <mutex>
 
@@ -20,6 +21,8 @@ using tk::kMaxK;
 using tk::kMaxSpanVecs;
 using tk::kMergeGroup;
 using tk::kVecElems;
+using tk::kSampleElems;
+using tk::kSpecFailure;
 
 constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;  // keeps grid work-items below 2^32
 constexpr int64_t kMinSpanCols = 4096;                      // a split never makes spans narrower
@@ -81,6 +84,25 @@ int32_t plan(int64_t rows, int64_t cols, int32_t compute_units) {
   if (s < need) s = need;
   if (s < 1) s = 1;
   return (int32_t)s;
+}
+
+// Rank j of the speculative floor in a workgroup's pooled sample (the first
+// chunk of each wave).  The floor T is the sample's j-th largest lane
+// maximum, at most its j-th largest element; it fails (fewer than k keys of
+// the span reach it) only if j sample elements lie among the span's k - 1
+// largest.  That count is about Poisson with mean k * sample / span, so j is
+// the smallest rank whose tail probability is at most kSpecFailure.  Returns
+// 0 when no rank below k qualifies (the exact floor, rank k, is then as good).
+int32_t spec_rank(int32_t k, int64_t span_cols) {
+  if (span_cols <= 0) return 0;
+  const double lambda = (double)k * (double)kSampleElems / (double)span_cols;
+  double p = std::exp(-lambda), cdf = p;  // P(X = 0), P(X <= 0)
+  for (int32_t j = 1; j < k; ++j) {
+    if (1.0 - cdf <= kSpecFailure) return j;  // P(X >= j)
+    p *= lambda / j;
+    cdf += p;
+  }
+  return 0;
 }
 
 std::atomic<int32_t> g_cu_count[64];
@@ -189,6 +211,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   sa.k = k;
   sa.spans = spans;
   sa.exact = exact;
+  sa.spec_rank = exact ? 0 : spec_rank(k, cols / spans);
   sa.out_idx = out_idx;
   sa.out_val = out_val;
   sa.out_count = out_count;

@@ -23,7 +23,8 @@ constexpr int kMergeGroup = 64;                // span lists one merge workgroup
 constexpr int kMergeThreads = 256;
 constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
-constexpr int kSpecMargin = 3;                 // the floor's sample rank targets this many times k keys
+constexpr int kSampleElems = 4 * 4 * 64 * 8;    // pooled sample: the first chunk of each wave
+constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
 
 static_assert(kMaxK == (int)TK_MAX_K, "public and internal max k differ");
 static_assert(kMaxK <= kWave, "a wave holds one kept entry per lane");
@@ -32,6 +33,7 @@ static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
 // edges of < kVecElems columns each; its columns must stay within 16 bits.
 static_assert(((kMaxSpanVecs + kWgWaves - 1) / kWgWaves) * kVecElems + 2 * kVecElems <= kMaxWaveCols,
               "a wave's column range must fit the 16-bit relative index");
+static_assert(kSampleElems == kWgWaves * kChunkVecs * kWave * kVecElems, "sample = one chunk per wave");
 static_assert(kMergeGroup * kMaxK * 8 * 2 <= 64 * 1024, "merge double buffer must fit LDS");
 
 }  // namespace tk

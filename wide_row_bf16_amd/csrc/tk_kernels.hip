@@ -244,7 +244,7 @@ struct WaveTopK {
   uint32_t list;   // lane i: i-th best composite so far, 0 = empty
   uint32_t kth;    // wave-uniform copy of list[k - 1]
   uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of other waves
-  uint32_t floor;  // wave-uniform speculative floor: only keys > floor are kept (0 = none)
+  uint32_t floor;  // wave-uniform floor: only keys > floor are kept (0 = none)
   uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
   int km1;         // k - 1
   int qm1;         // ceil(k / 4) - 1
@@ -520,33 +520,29 @@ __device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4
   }
 }
 
-// The j-th largest of the 64 per-lane maximum order keys of this wave's first
-// chunk (vectors [0, kChunkVecs * 64) of the nvec at vp; NaN counts as key 0),
-// j <= 64.  At least j elements of the chunk reach it, and for j much smaller
-// than 64 it is about the j-th largest key of the chunk.  Used to pick a
-// speculative floor; see span_scan_kernel.
-__device__ __forceinline__ uint32_t first_chunk_key(const uint4 *vp, uint32_t nvec, int j, const Xchg &x) {
-  uint4 v[kChunkVecs];
-  load_chunk(v, vp, nvec, 0, (uint32_t)lane_id() * 16u);
+// This lane's largest order key in a loaded chunk (vectors [first, first +
+// kChunkVecs * 64) of nvec; vectors at or past nvec count as key 0, as does
+// NaN).  Sorted over the wave, these give the floors of span_scan_kernel.
+__device__ __forceinline__ uint32_t lane_max_key(const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec) {
   uint32_t m = 0;
 #pragma unroll
   for (int u = 0; u < kChunkVecs; ++u) {
     const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t mu = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = max(m, order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+    for (int e = 0; e < 8; ++e) mu = max(mu, order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+    if (first + (uint32_t)(u * kWave + lane_id()) < nvec) m = max(m, mu);
   }
-  // the caller only asks when the first chunk is full
-  return readlane(sort64_desc(m, x), j - 1);
+  return m;
 }
 
 // Streams nvec 16-byte vectors starting at vp (its first element is column
-// col_first), two chunks in flight.
+// col_first), two chunks in flight.  A holds the first chunk, already loaded.
 __device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t nvec, int64_t col_first,
-                                          int64_t base) {
+                                          int64_t base, uint4 (&A)[kChunkVecs]) {
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;  // vectors per chunk
   const uint32_t lane_off = (uint32_t)lane_id() * 16u;
-  uint4 A[kChunkVecs], B[kChunkVecs];
-  load_chunk(A, vp, nvec, 0, lane_off);
+  uint4 B[kChunkVecs];
   for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
     load_chunk(B, vp, nvec, first + kStep, lane_off);
     take_chunk(w, A, first, nvec, col_first, base);
@@ -589,7 +585,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   __shared__ int32_t s_count[kWgWaves];
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
-  __shared__ uint32_t s_t0[kWgWaves];
+  __shared__ uint32_t s_samp[kWgWaves][kWave];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -619,30 +615,44 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
   const int64_t base = (wave == 0 && head_hi > head_lo) ? head_lo : a0 + kVecElems * wv0;
 
-  // Speculative floor.  When every wave's share spans at least kSpecChunks
-  // chunks, each wave takes a high key T_w from a sample (its first chunk)
-  // and the workgroup keeps only keys >= T0 = min T_w.  T_w is the sample's
-  // j-th largest (about), with j chosen so that about kSpecMargin * k keys of
-  // the span are expected to reach it.  The result is verified: if the lists
-  // end with k entries (all >= T0), every dropped element is beaten by k kept
-  // ones and the answer is exact; otherwise the span is scanned again without
-  // a floor, which the margin makes rare.
-  uint32_t floor = 0;
-  const bool speculate = !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
-  if (speculate) {
-    // expected keys of the span >= the sample's j-th largest: j * 8 n / sample
-    constexpr int64_t kSample = (int64_t)kChunkVecs * kWave * kVecElems;
-    const int64_t want = (int64_t)kSpecMargin * a.k * kSample;
-    int j = (int)((want + kVecElems * n - 1) / (kVecElems * n));
-    j = j < 2 ? 2 : (j > kWave ? kWave : j);
-    const uint32_t t = first_chunk_key(reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), j,
-                                       make_xchg());
-    if (l == 0) s_t0[wave] = t;
+  // Floors from a sample: the first chunk of each wave, loaded here and handed
+  // on to take_body.  Each wave sorts its 64 per-lane maximum keys; every wave
+  // then merges the four sorted lists into the top 64 of the 256 (the same
+  // result in every wave).  Two floors follow:
+  //  - exact: the k-th largest lane maximum T has k elements (one per lane) at
+  //    or above it, so no key below T can be among the top k of the span; only
+  //    keys >= T are kept.  This spares young lists most of their filling.
+  //  - speculative (rank j = spec_rank < k, chosen on the host from k and the
+  //    span width, and only when every wave's share spans at least kSpecChunks
+  //    chunks): the j-th largest lane maximum, about the sample's j-th largest
+  //    key.  The result is verified: if the lists end with k entries (all
+  //    above that floor), every dropped element is beaten by k kept ones and
+  //    the answer is exact; otherwise the span is scanned again under the
+  //    exact floor, which the choice of j makes rare.
+  uint32_t exact_floor = 0, spec_floor = 0;
+  const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t wn = (uint32_t)(wv1 - wv0);
+  uint4 A[kChunkVecs];
+  if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
+  const bool speculate =
+      a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
+  {
+    const Xchg x = make_xchg();
+    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn) : 0u, x);
     __syncthreads();
-    uint32_t t0 = s_t0[0];
-#pragma unroll
-    for (int o = 1; o < kWgWaves; ++o) t0 = min(t0, s_t0[o]);
-    floor = t0 > 0 ? t0 - 1 : 0;
+    const uint32_t m01 = bitonic_merge64_desc(max(s_samp[0][l], partner<63>(s_samp[1][l], x)), x);
+    const uint32_t m23 = bitonic_merge64_desc(max(s_samp[2][l], partner<63>(s_samp[3][l], x)), x);
+    const uint32_t top = bitonic_merge64_desc(max(m01, partner<63>(m23, x)), x);
+    const uint32_t te = readlane(top, a.k - 1);
+    const uint32_t ts = speculate ? readlane(top, a.spec_rank - 1) : 0u;
+    exact_floor = te > 0 ? te - 1 : 0;
+    spec_floor = ts > 0 ? ts - 1 : 0;
+  }
+  uint32_t floor = exact_floor;
+  bool verify = false;
+  if (spec_floor > exact_floor) {
+    floor = spec_floor;
+    verify = true;
   }
 
   int total = 0;
@@ -663,8 +673,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     w.x = make_xchg();
 
     if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
-    if (wv1 > wv0)
-      take_body(w, reinterpret_cast<const uint4 *>(row + a0) + wv0, (uint32_t)(wv1 - wv0), a0 + kVecElems * wv0, base);
+    if (wn > 0) take_body(w, wvp, wn, a0 + kVecElems * wv0, base, A);
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns(w, row, tail_lo, tail_hi, base);
 
     // publish this wave's list
@@ -684,9 +693,12 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
       total += s_count[o];
       flags |= s_flags[o];
     }
-    if (floor == 0 || total >= a.k) break;  // exact, or the speculation verified
-    floor = 0;                              // too few entries reach T0: scan again without it
-    __syncthreads();                        // every wave has read the counts above
+    if (!verify || total >= a.k) break;  // exact, or the speculation verified
+    // too few entries reach the speculative floor: scan again under the exact one
+    floor = exact_floor;
+    verify = false;
+    if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
+    __syncthreads();  // every wave has read the counts above
   }
   if (total > a.k) total = a.k;
 

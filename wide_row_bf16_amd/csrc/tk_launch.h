@@ -19,6 +19,7 @@ struct ScanArgs {
   int32_t k;
   int32_t spans;
   int32_t exact;        // 1: never use a speculative floor
+  int32_t spec_rank;    // rank (1-based) of the speculative floor in the pooled sample; 0: none
   int32_t *out_idx;
   uint16_t *out_val;
   int32_t *out_count;
