@@ -63,6 +63,7 @@ __device__ __forceinline__ uint64_t lanes_sgt(int32_t a, int32_t b) { return __b
 __device__ __forceinline__ uint64_t lanes_ugt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 34); }
 __device__ __forceinline__ uint64_t lanes_uge(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 35); }
 __device__ __forceinline__ uint64_t lanes_ult(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36); }
+__device__ __forceinline__ uint64_t lanes_eq(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 32); }
 
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
@@ -254,7 +255,10 @@ struct WaveTopK {
 };
 
 // Adds the candidates c of lanes m (their composites beat the k-th) to the
-// list: one bitonic batch when many, else one insertion each.
+// list: one bitonic batch when many, else one insertion each.  Insertions
+// test against a copy of the k-th that is refreshed only afterwards: a stale
+// (lower) k-th only lets extra candidates through, and inserting one that no
+// longer qualifies changes list slots >= k only.
 __device__ __forceinline__ void offer(WaveTopK &w, uint32_t c, uint64_t m) {
   if (__popcll(m) >= kBatchInsert) {
     w.list = merge_batch(w.list, c > w.kth ? c : 0u, w.x);
@@ -262,23 +266,10 @@ __device__ __forceinline__ void offer(WaveTopK &w, uint32_t c, uint64_t m) {
     do {
       const int l = __builtin_ctzll(m);
       m &= m - 1;
-      w.list = insert_one(w.list, readlane(c, l));  // stale k-th: see take_one
+      w.list = insert_one(w.list, readlane(c, l));
     } while (m);
   }
   w.kth = readlane(w.list, w.km1);
-}
-
-// One element whose bits b (wave-uniform) may beat the k-th or carry an
-// unflagged -inf / NaN; inv = 0xFFFF - (column - wave base).  NaN gets key 0,
-// which never exceeds ext, so it is flagged and never kept.  The k-th copy is
-// not refreshed here: testing later hits of the same batch against a stale
-// (lower) k-th only lets extra candidates through, and inserting one that no
-// longer qualifies changes list slots >= k only.
-__device__ __forceinline__ void take_one(WaveTopK &w, uint32_t b, uint32_t inv) {
-  const uint32_t key = order_key(b);
-  w.flags |= key == 0 ? kNan : (b == 0xFF80u ? kNinf : 0u);
-  const uint32_t c = (key << 16) | (inv & 0xFFFFu);
-  if (key > w.ext && c > w.kth) w.list = insert_one(w.list, c);
 }
 
 // Threshold sharing between the waves of a workgroup.  Each wave publishes
@@ -338,30 +329,30 @@ __device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
 __device__ __forceinline__ v2i16 as_i16x2(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
 __device__ __forceinline__ v2u16 as_u16x2(uint32_t x) { return __builtin_bit_cast(v2u16, x); }
 
-// trip[u]: the lanes whose vector u holds an element whose key may exceed T
-// or that carries an unflagged -inf / NaN.  (Never a false negative; a false
-// positive only costs the exact path.)
+// vt[u]: the lanes whose vector u holds an element whose key may exceed T;
+// ft[u]: the lanes whose vector u holds a -inf / NaN pattern not flagged yet.
+// (Never a false negative; a false positive only costs the exact path.)
 template <int N>
-__device__ __forceinline__ void lane_trips(const uint4 (&v)[N], const Filter &f, uint64_t (&trip)[N]) {
+__device__ __forceinline__ void lane_trips(const uint4 (&v)[N], const Filter &f, uint64_t (&vt)[N], uint64_t (&ft)[N]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
+                                              __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
+    ft[u] = lanes_uge(max((uint32_t)h.x, (uint32_t)h.y), f.ftrip);
+  }
   if (f.nonneg) {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const v2i16 a = __builtin_elementwise_max(__builtin_elementwise_max(as_i16x2(v[u].x), as_i16x2(v[u].y)),
                                                 __builtin_elementwise_max(as_i16x2(v[u].z), as_i16x2(v[u].w)));
-      const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
-                                                __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
-      trip[u] = lanes_sgt(max((int32_t)a.x, (int32_t)a.y), f.t16) |
-                lanes_uge(max((uint32_t)h.x, (uint32_t)h.y), f.ftrip);
+      vt[u] = lanes_sgt(max((int32_t)a.x, (int32_t)a.y), f.t16);
     }
   } else {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const v2u16 lo = __builtin_elementwise_min(__builtin_elementwise_min(as_u16x2(v[u].x), as_u16x2(v[u].y)),
                                                  __builtin_elementwise_min(as_u16x2(v[u].z), as_u16x2(v[u].w)));
-      const v2u16 h = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(v[u].x), as_u16x2(v[u].y)),
-                                                __builtin_elementwise_max(as_u16x2(v[u].z), as_u16x2(v[u].w)));
-      trip[u] = lanes_ult(min((uint32_t)lo.x, (uint32_t)lo.y), f.tu) |
-                lanes_uge(max((uint32_t)h.x, (uint32_t)h.y), f.ftrip);
+      vt[u] = lanes_ult(min((uint32_t)lo.x, (uint32_t)lo.y), f.tu);
     }
   }
 }
@@ -396,35 +387,53 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
   }
 }
 
-// Exact path for one 16-byte vector when few lanes trip: the eight
-// per-element predicates over all lanes are evaluated back to back against
-// the vector's starting thresholds (a conservative pre-test: they only rise),
-// then the hit masks are walked with wave-uniform arithmetic.  NONNEG selects
-// the filter form (int16 compare for T >= 0, uint16 compare for T < 0).
-// inv_l0 is 0xFFFF - rel of element 0 of lane 0's vector; lane l's vector
-// starts 8 l columns later.
+// Exact path for one 16-byte vector per lane when few lanes trip: the eight
+// per-element tests against T on the raw bits (lanes `valid`; a conservative
+// pre-test, since T only rises), then for each element position with hits the
+// composites of all lanes at once and one insertion per hit.  NONNEG selects
+// the filter form: for T >= 0 only non-negative bit patterns can pass, whose
+// key is bits + 0x8000.  NaN patterns that pass are flagged, never kept.
+// inv0 = 0xFFFF - rel of this lane's element 0.
 template <bool NONNEG>
-__device__ __forceinline__ void take_lanes_ballot(WaveTopK &w, uint4 d, uint32_t inv_l0, uint64_t valid,
-                                                  const Filter &f) {
+__device__ __forceinline__ void take_lanes_value(WaveTopK &w, uint4 d, uint32_t inv0, uint64_t valid, const Filter &f) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
   uint64_t m[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
-    const uint64_t beats = NONNEG ? lanes_sgt((int32_t)(int16_t)b, f.t16) : lanes_ult(b, f.tu);
-    m[e] = (beats | lanes_uge(b, f.ftrip)) & valid;
+    m[e] = (NONNEG ? lanes_sgt((int32_t)(int16_t)b, f.t16) : lanes_ult(b, f.tu)) & valid;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    while (m[e]) {
-      const int l = __builtin_ctzll(m[e]);
-      m[e] &= m[e] - 1;
-      const uint32_t wl = readlane(dw[e >> 1], l);
-      take_one(w, (e & 1) ? wl >> 16 : wl & 0xFFFFu, inv_l0 - (uint32_t)(kVecElems * l + e));
+    if (!m[e]) continue;
+    const uint32_t word = dw[e >> 1];
+    const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
+    const uint32_t key = NONNEG ? (b > 0x7F80u ? 0u : b | 0x8000u) : order_key(b);
+    if (m[e] & lanes_eq(key, 0u)) w.flags |= kNan;
+    const uint32_t c = key ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
+    uint64_t h = m[e] & lanes_ugt(c, w.kth);
+    while (h) {  // against a stale k-th: see offer
+      const int l = __builtin_ctzll(h);
+      h &= h - 1;
+      w.list = insert_one(w.list, readlane(c, l));
     }
   }
   w.kth = readlane(w.list, w.km1);
+}
+
+// Flags the -inf / NaN patterns at or above ftrip in the vectors of lanes
+// `lanes`; nothing is kept here (a -inf that can be kept also passes T).
+__device__ __forceinline__ void take_flags(WaveTopK &w, uint4 d, uint64_t lanes, uint32_t ftrip) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t word = dw[e >> 1];
+    const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
+    const uint64_t m = lanes_uge(b, ftrip) & lanes;
+    if (m & lanes_eq(b, 0xFF80u)) w.flags |= kNinf;
+    if (m & lanes_ugt(b, 0xFF80u)) w.flags |= kNan;
+  }
 }
 
 constexpr int kDenseLanes = 16;  // this many tripping lanes pick the dense path
@@ -460,10 +469,11 @@ constexpr int kLoadPolicy = 2;
 __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                            int64_t col_first, int64_t base) {
   w.ext = max(shared_bound(w.tau, w.wave), w.floor);
-  uint64_t trip[kChunkVecs];
-  lane_trips<kChunkVecs>(v, make_filter(w), trip);
+  const Filter f0 = make_filter(w);
+  uint64_t vt[kChunkVecs], ft[kChunkVecs];
+  lane_trips<kChunkVecs>(v, f0, vt, ft);
   static_assert(kChunkVecs == 4, "rotation below");
-  if (!(trip[0] | trip[1] | trip[2] | trip[3])) return;
+  if (!(vt[0] | vt[1] | vt[2] | vt[3] | ft[0] | ft[1] | ft[2] | ft[3])) return;
   const uint32_t l = (uint32_t)lane_id();
   uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // rotated once per vector below
   // 0xFFFF - rel of element 0 of this lane's vector (first + l)
@@ -472,24 +482,32 @@ __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkV
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
     const uint64_t valid = lanes_ult(vi, nvec);
-    const uint64_t m = trip[0] & valid;
-    if (m) {
+    const uint64_t mv = vt[0] & valid, mf = ft[0] & valid;
+    if (mv | mf) {
       const uint4 d = x0;
-      if (__popcll(m) >= kDenseLanes) {
+      if (__popcll(mv | mf) >= kDenseLanes) {
         take_vector_dense(w, d, inv0, vi < nvec);
         // the young set just grew a lot: share it and take the others' news
         publish(w.tau, w.wave, w);
         w.ext = max(shared_bound(w.tau, w.wave), w.floor);
       } else {
-        const Filter f = make_filter(w);
-        const uint32_t inv_l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(inv0 + (uint32_t)kVecElems * l));
-        if (f.nonneg) take_lanes_ballot<true>(w, d, inv_l0, valid, f);
-        else take_lanes_ballot<false>(w, d, inv_l0, valid, f);
+        if (mf) take_flags(w, d, mf, f0.ftrip);
+        if (mv) {
+          const Filter f = make_filter(w);
+          if (f.nonneg) take_lanes_value<true>(w, d, inv0, mv, f);
+          else take_lanes_value<false>(w, d, inv0, mv, f);
+        }
       }
     }
-    trip[0] = trip[1];
-    trip[1] = trip[2];
-    trip[2] = trip[3];
+    vt[0] = vt[1];
+    vt[1] = vt[2];
+    vt[2] = vt[3];
+    vt[3] = 0;
+    ft[0] = ft[1];
+    ft[1] = ft[2];
+    ft[2] = ft[3];
+    ft[3] = 0;
+    if (!(vt[0] | vt[1] | vt[2] | ft[0] | ft[1] | ft[2])) break;
     x0 = x1;
     x1 = x2;
     x2 = x3;
@@ -543,7 +561,16 @@ __device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;  // vectors per chunk
   const uint32_t lane_off = (uint32_t)lane_id() * 16u;
   uint4 B[kChunkVecs];
+  // Issue priority falls with progress (3 in the first quarter of the share,
+  // 0 in the last): a SIMD otherwise favours its oldest waves, which then run
+  // ahead while the youngest lag, and the kernel ends in a tail with too few
+  // waves left to keep HBM busy.  Waves that are behind now issue first.
+  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;
+  __builtin_amdgcn_s_setprio(3);
   for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+    if (first >= q3) __builtin_amdgcn_s_setprio(0);
+    else if (first >= q2) __builtin_amdgcn_s_setprio(1);
+    else if (first >= q1) __builtin_amdgcn_s_setprio(2);
     load_chunk(B, vp, nvec, first + kStep, lane_off);
     take_chunk(w, A, first, nvec, col_first, base);
     if (first + kStep >= nvec) break;
