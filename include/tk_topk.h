@@ -32,7 +32,10 @@
  * keeps no pointer after the call returns; the caller keeps the buffers alive
  * until the stream has passed the call.  Calls on different streams may run
  * concurrently.  Temporary span lists are stream-ordered allocations of the
- * library (hipMallocAsync / hipFreeAsync on `stream`).
+ * library (hipMallocAsync / hipFreeAsync on `stream`), kept per stream between
+ * calls; calls that overlap on one stream cannot happen (the stream orders
+ * them), and the buffer's per-row merge counters return to zero at the end of
+ * every call.
  *
  * Errors: the guards below run on the host before any device work; on a
  * guard error nothing is launched and nothing is written.  TK_ERR_DEVICE
@@ -85,7 +88,8 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
  * them: every plan computes the same bytes.
  *   spans  0 = automatic; 1 = one workgroup scans each whole row (the
  *          single-group control); n > 1 = split each row into n spans whose
- *          candidate lists a second dispatch merges.  Rejected with
+ *          candidate lists are merged in the same order: by the row's last
+ *          scan workgroup for n <= 64, by merge dispatches above.  Rejected with
  *          TK_ERR_OPTION when a span would exceed the library's span limit
  *          (tk_max_span_cols()) or n > cols (for cols > 0).
  *   exact  0 = automatic; 1 = never take the speculative floor (wide spans

@@ -117,3 +117,28 @@ def test_many_rows():
         from gpu_util import check_case
 
         check_case(m, cols, k, what=f"{rows}x{cols}")
+
+
+def test_fused_merge_state_across_calls_and_batches():
+    """Split rows are folded by the last scan workgroup of each row, which
+    counts arrivals in per-row counters that must return to zero after every
+    call.  Alternating shapes on one stream, several row batches in one call
+    (more split rows than one launch takes) and span counts on both sides of
+    the fused limit (64) must all give the oracle's bytes."""
+    cases = [
+        ("normal", 15, 98592, 32, 0),
+        ("mixed_nonfinite", 40, 20000, 7, 5),
+        ("levels64", 15, 98592, 32, 64),
+        ("uniform_bits", 3, 98592, 64, 65),
+        ("logit", 15, 98592, 32, 0),
+        ("zeros_straddle", 9000, 128, 4, 2),
+        ("normal", 15, 98592, 32, 18),
+    ]
+    for family, rows, cols, k, spans in cases:
+        m = family_rows(family, rows, cols, cols + 3, seed=rows + spans)
+        log(f"fused family={family} rows={rows} cols={cols} k={k} spans={spans}")
+        want = oracle.topk_bf16(m, cols, k)
+        from gpu_util import gpu_topk
+
+        for _ in range(2):
+            assert_same(gpu_topk(m, cols, k, spans=spans), want, f"{family} {rows}x{cols} k={k} spans={spans}")

@@ -20,13 +20,19 @@ namespace {
 using tk::kMaxK;
 using tk::kMaxSpanVecs;
 using tk::kMergeGroup;
+using tk::kFusedMaxRows;
 using tk::kVecElems;
 using tk::kSampleElems;
 using tk::kSpecFailure;
 
 constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;  // keeps grid work-items below 2^32
 constexpr int64_t kMinSpanCols = 4096;                      // a split never makes spans narrower
-constexpr int32_t kMaxAutoSpans = 64;                       // automatic plans fold in one merge level
+// Automatic plans use at most 12 spans per row (unless the span width limit
+// needs more): the row's last workgroup folds the span lists in a chain of
+// about S / 4 + 3 merges, and on few-row inputs 8-12 spans measured fastest
+// (15 x 98592: 13.8 us at 8-12 spans, 15.6 us at 18; 16 x 248320: 17.6 us at
+// 12, 18.0 us at 16).
+constexpr int32_t kMaxAutoSpans = 12;
 constexpr int32_t kMaxSpans = 1 << 16;
 
 struct Range {
@@ -154,8 +160,11 @@ int g_scratch_used = 0;
 
 // With g_scratch_mu held: a cached buffer of at least `bytes` for (dev,
 // stream), or nullptr when the request is not cached (the caller allocates).
-void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st) {
+// *fresh tells that the buffer was just allocated (its contents are
+// undefined).
+void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st, bool *fresh) {
   *st = TK_OK;
+  *fresh = false;
   if (bytes > kCacheMaxBytes) return nullptr;
   ScratchSlot *slot = nullptr;
   for (int i = 0; i < g_scratch_used; ++i)
@@ -177,6 +186,7 @@ void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st) {
     }
     if (*st != TK_OK) return nullptr;
     slot->cap = cap;
+    *fresh = true;
   }
   return slot->ptr;
 }
@@ -227,12 +237,20 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
     return TK_OK;
   }
 
-  // Scratch for one batch of rows: the span lists, then each merge level's lists.
-  const int64_t batch = rows < rows_per_launch ? rows : rows_per_launch;
+  // Scratch for one batch of rows: the fused merge's arrival counters (always
+  // at offset 0, so that they keep their all-zero state between calls whatever
+  // the shapes), then the span lists, then each merge level's lists.  With at
+  // most kMergeGroup spans and kFusedMaxRows rows per launch the scan folds
+  // the span lists itself (one dispatch); otherwise merge dispatches follow.
+  const bool fused = spans <= kMergeGroup && rows_per_launch >= 1;
+  const int64_t batch_cap = fused && rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
+  const int64_t batch = rows < batch_cap ? rows : batch_cap;
   int32_t level_lists[8];
   int levels = 0;
   for (int32_t n = spans; n > 1; n = (n + kMergeGroup - 1) / kMergeGroup) level_lists[levels++] = n;
-  size_t off_list[8], off_count[8], off_flags[8], total = 0;
+  if (fused) levels = 1;  // only the span lists
+  const size_t counters_bytes = align256((size_t)kFusedMaxRows * sizeof(int32_t));
+  size_t off_list[8], off_count[8], off_flags[8], total = counters_bytes;
   for (int i = 0; i < levels; ++i) {
     const size_t nlists = (size_t)batch * (size_t)level_lists[i];
     off_list[i] = total;
@@ -245,28 +263,41 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   keep_pool(dev);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   tk_status sst = TK_OK;
-  void *scratch = cached_scratch(dev, stream, total, &sst);
+  bool fresh = false;
+  void *scratch = cached_scratch(dev, stream, total, &sst, &fresh);
   if (sst != TK_OK) return sst;
   const bool owned = scratch == nullptr;
   if (owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
   char *base = (char *)scratch;
+  int32_t *counters = (int32_t *)base;
+  if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
+    if (owned) hipFreeAsync(scratch, stream);
+    return TK_ERR_DEVICE;
+  }
 
   tk_status result = TK_OK;
   for (int64_t r0 = 0; r0 < rows && result == TK_OK; r0 += batch) {
     const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
     // Scratch rows are indexed from the batch start: point the row-indexed
-    // outputs of the scan at the batch, and offset the input by r0 rows.
+    // outputs at the batch, and offset the input by r0 rows.
     tk::ScanArgs b = sa;
     b.in = in + r0 * stride;
     b.row0 = 0;
     b.span_list = (uint64_t *)(base + off_list[0]);
     b.span_count = (int32_t *)(base + off_count[0]);
     b.span_flags = (uint32_t *)(base + off_flags[0]);
+    if (fused) {
+      b.row_done = counters;
+      b.out_idx = out_idx + r0 * k;
+      b.out_val = out_val + r0 * k;
+      b.out_count = out_count + r0;
+      b.out_nonfinite = out_nonfinite + r0;
+    }
     if (tk::launch_span_scan(b, nr, stream) != hipSuccess) {
       result = TK_ERR_DEVICE;
       break;
     }
-    for (int i = 0; i < levels; ++i) {
+    for (int i = 0; i < levels && !fused; ++i) {
       tk::MergeArgs m{};
       m.in = in + r0 * stride;
       m.row0 = 0;

@@ -21,6 +21,7 @@ constexpr int64_t kMaxSpanVecs = 32640;        // 16-byte vectors one workgroup 
 constexpr int64_t kMaxSpanCols = kMaxSpanVecs * kVecElems;  // 261120
 constexpr int kMergeGroup = 64;                // span lists one merge workgroup folds at most
 constexpr int kMergeThreads = 256;
+constexpr int kFusedMaxRows = 4096;             // rows per launch of the fused (single-dispatch) split path
 constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
 constexpr int kSampleElems = 4 * 4 * 64 * 8;    // pooled sample: the first chunk of each wave

@@ -63,6 +63,7 @@ __device__ __forceinline__ uint64_t lanes_sgt(int32_t a, int32_t b) { return __b
 __device__ __forceinline__ uint64_t lanes_ugt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 34); }
 __device__ __forceinline__ uint64_t lanes_uge(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 35); }
 __device__ __forceinline__ uint64_t lanes_ult(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36); }
+constexpr int kAgent = __HIP_MEMORY_SCOPE_AGENT;
 __device__ __forceinline__ uint64_t lanes_eq(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 32); }
 
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
@@ -607,6 +608,88 @@ __device__ __forceinline__ int count_beating(const uint64_t *list, int n, uint64
   return lo;
 }
 
+// Fused merge of a split row.  Every scan workgroup of row r has written its
+// span list; the last one to arrive folds all S lists into the row's outputs,
+// with the order and rules of span_merge_kernel, and resets the row's counter
+// to zero for the next call on the stream.  The lists, counts and flags are
+// written and read with agent-scope atomic accesses, which bypass the
+// non-coherent cache levels (each XCD has its own L2), so no cache writeback
+// or invalidation is needed: a workgroup waits until its stores have
+// completed, then counts its arrival; the last arrival reads every list.
+__device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, int S, const uint16_t *row, int wave,
+                                              int l) {
+  __shared__ int s_last;
+  __shared__ uint64_t s_acc[kWgWaves][kWave];
+  __shared__ int32_t s_cnt[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+  const int64_t rb = r - a.row0;  // the row's counter within this launch
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's list stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const Xchg x = make_xchg();
+  uint64_t acc = 0;
+  int cnt = 0;
+  uint32_t fl = 0;
+  // each wave folds lists wave, wave + 4, ...; four lists' loads in flight at once
+  for (int i0 = wave; i0 < S; i0 += 4 * kWgWaves) {
+    uint64_t v[4];
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kWgWaves;
+      const int64_t sb = r * S + i;
+      c[j] = 0;
+      v[j] = 0;
+      if (i < S) {
+        c[j] = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent);
+        fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
+        if (l < a.k) v[j] = __hip_atomic_load(&a.span_list[sb * a.k + l], __ATOMIC_RELAXED, kAgent);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j * kWgWaves >= S) break;
+      const uint64_t vj = l < c[j] ? v[j] : 0;
+      acc = (i0 == wave && j == 0) ? vj : merge_sorted64(acc, vj, x);
+      cnt += c[j];
+    }
+  }
+  s_acc[wave][l] = acc;
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_fl[wave] = fl;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int o = 1; o < kWgWaves; ++o) {
+      acc = merge_sorted64(acc, s_acc[o][l], x);
+      cnt += s_cnt[o];
+      fl |= s_fl[o];
+    }
+    const int k = a.k;
+    if (cnt > k) cnt = k;
+    const int64_t ob = r * k;
+    if (l < k) {
+      if (l < cnt) {
+        a.out_idx[ob + l] = col_of(acc);
+        a.out_val[ob + l] = value_bits(acc, row);
+      } else {
+        a.out_idx[ob + l] = TK_FILL_IDX;
+        a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;
+      }
+    }
+    if (l == 0) {
+      a.out_count[r] = cnt;
+      a.out_nonfinite[r] = fl;
+      __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   __shared__ uint64_t s_list[kWgWaves][kWave];
   __shared__ int32_t s_count[kWgWaves];
@@ -754,12 +837,14 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
       a.out_nonfinite[r] = flags;
     }
   } else {
+    // agent-scope stores: coherent across the XCDs' caches (see fold_row_if_last)
     const int64_t sb = r * S + s;
-    if (mine && rank < a.k) a.span_list[sb * a.k + rank] = x;
+    if (mine && rank < a.k) __hip_atomic_store(&a.span_list[sb * a.k + rank], x, __ATOMIC_RELAXED, kAgent);
     if (threadIdx.x == 0) {
-      a.span_count[sb] = total;
-      a.span_flags[sb] = flags;
+      __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
+      __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
     }
+    if (a.row_done) fold_row_if_last(a, r, S, row, wave, l);
   }
 }
 
@@ -845,6 +930,17 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
 }
 
 }  // namespace
+
+__global__ void zero_fill_kernel(int32_t *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream) {
   const int64_t blocks = rows_in_launch * a.spans;

@@ -10,7 +10,9 @@ namespace tk {
 // One scan workgroup per (row, span).  Rows [row0, row0 + rows_in_launch) of
 // the matrix are covered by rows_in_launch * spans workgroups.  With spans == 1
 // the scan writes the final outputs; otherwise it writes one sorted candidate
-// list per (row, span) into the span arrays for the merge dispatch.
+// list per (row, span) into the span arrays, for the merge dispatch or, with
+// row_done set, for the row's last workgroup to fold (fused merge: spans <=
+// kMergeGroup, rows_in_launch <= kFusedMaxRows).
 struct ScanArgs {
   const uint16_t *in;
   int64_t row0;
@@ -27,6 +29,7 @@ struct ScanArgs {
   uint64_t *span_list;  // [rows][spans][k] composite (key << 32 | ~col), descending
   int32_t *span_count;  // [rows][spans]
   uint32_t *span_flags; // [rows][spans]
+  int32_t *row_done;    // non-NULL: fused merge; per-row arrival counters, zero between calls
 };
 
 // One merge workgroup per (row, group of up to kMergeGroup input lists).
@@ -53,5 +56,6 @@ struct MergeArgs {
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
+hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
 
 }  // namespace tk
