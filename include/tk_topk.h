@@ -120,6 +120,51 @@ tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32
  */
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units);
 
+/*
+ * Vocabulary-sharded top-k.  The split of a wide row into spans whose
+ * candidate lists are merged in the same (score desc, lower index first) order
+ * (TensorFold PR #713, change 3) carried across devices: each device holds a
+ * column shard of every row, finds the shard's top k, and one merge over the
+ * gathered shard results gives the row's top k.  (The pages run one rank; the
+ * cross-device use is this library's plain reading of the span split.)
+ *
+ * tk_topk_bf16_shard: tk_topk_bf16 on a shard whose column 0 is the row's
+ * global column col_base; out_idx holds global indices (col_base + local).
+ * Requires col_base >= 0 and col_base + cols - 1 <= INT32_MAX
+ * (TK_ERR_SHAPE otherwise); all else as tk_topk_bf16.
+ */
+tk_status tk_topk_bf16_shard(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, int64_t col_base,
+                             const uint16_t *in, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
+                             uint32_t *out_nonfinite, void *stream);
+
+#define TK_MAX_SHARDS 4096
+
+/*
+ * tk_merge_topk_bf16: the top k of each row over `shards` shard results, in
+ * the same order.  Inputs are the shards' outputs stacked shard-major, the
+ * layout an all-gather of dense per-shard blocks produces (all device
+ * memory):
+ *   idx_in, val_in     [shards][rows][k]   entries as tk_topk_bf16_shard wrote
+ *                                          them (global indices, bf16 bits)
+ *   count_in, mask_in  [shards][rows]      per-shard counts and non-finite masks
+ * Outputs as tk_topk_bf16: count = min(k, sum of the shard counts), mask = OR
+ * of the shard masks, entries in order, fill after count.  Every shard must
+ * have used this k.  1 <= shards <= TK_MAX_SHARDS (else TK_ERR_SHAPE).
+ * Guards as tk_topk_bf16 (NULL, alignment, outputs overlapping each other or
+ * an input -> TK_ERR_ALIAS); entries are trusted as written by
+ * tk_topk_bf16_shard (no memory is addressed through them).  Asynchronous on
+ * `stream`; no scratch memory.
+ */
+tk_status tk_merge_topk_bf16(int64_t rows, int32_t shards, int32_t k, const int32_t *idx_in, const uint16_t *val_in,
+                             const int32_t *count_in, const uint32_t *mask_in, int32_t *out_idx, uint16_t *out_val,
+                             int32_t *out_count, uint32_t *out_nonfinite, void *stream);
+
+/* The host-side guards of tk_merge_topk_bf16 alone (no HIP call). */
+tk_status tk_validate_merge_bf16(int64_t rows, int32_t shards, int32_t k, const int32_t *idx_in,
+                                 const uint16_t *val_in, const int32_t *count_in, const uint32_t *mask_in,
+                                 const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
+                                 const uint32_t *out_nonfinite);
+
 int32_t tk_max_k(void);             /* == TK_MAX_K */
 int64_t tk_max_span_cols(void);     /* widest span one workgroup scans */
 const char *tk_status_string(tk_status s);

@@ -118,3 +118,37 @@ def test_oracle_and_library_share_nothing():
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "tk_oracle" not in text, f
+
+
+# Shard merge inputs [shards][rows][k] and outputs, at separated fake addresses.
+M_IDX, M_VAL, M_CNT, M_MSK = 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+
+def vm(rows=3, shards=4, k=8, idx=M_IDX, val=M_VAL, cnt=M_CNT, msk=M_MSK, oidx=IDX, oval=VAL, ocnt=CNT, omsk=MSK):
+    return tk.validate_merge(rows, shards, k, idx, val, cnt, msk, oidx, oval, ocnt, omsk)
+
+
+def test_merge_guards():
+    assert vm() == OK
+    assert vm(rows=0, idx=None, val=None, cnt=None, msk=None, oidx=None, oval=None, ocnt=None, omsk=None) == OK
+    assert vm(shards=1) == OK and vm(shards=4096) == OK
+    assert vm(shards=0) == SHAPE and vm(shards=4097) == SHAPE and vm(rows=-1) == SHAPE
+    assert vm(k=0) == K and vm(k=65) == K
+    assert vm(val=None) == NULL and vm(omsk=None) == NULL
+    assert vm(val=M_VAL + 1) == ALIGN and vm(idx=M_IDX + 2) == ALIGN and vm(ocnt=CNT + 2) == ALIGN
+    # an output inside an input, or two outputs overlapping: rejected
+    assert vm(oidx=M_IDX + 64) == ALIAS
+    assert vm(oval=IDX + 8) == ALIAS
+    # inputs may share memory (they are only read)
+    assert vm(cnt=M_IDX, msk=M_IDX) == OK
+
+
+def test_shard_col_base_guard():
+    """Global indices must fit int32: rejected on the host before any HIP call."""
+    lib = tk.load()
+    args = (3, 100, 100, 8)
+    bufs = (IN, IDX, VAL, CNT, MSK, 0)
+    assert lib.tk_topk_bf16_shard(*args, -1, *bufs) == SHAPE
+    assert lib.tk_topk_bf16_shard(*args, 2**31 - 100 + 1, *bufs) == SHAPE
+    # rows == 0 returns before any device work; the largest valid base passes the guard
+    assert lib.tk_topk_bf16_shard(0, 100, 100, 8, 2**31 - 100, *bufs) == OK

@@ -33,8 +33,8 @@ FILL_IDX, FILL_VAL = -1, 0x7FC0
 
 # Every symbol the public header declares.
 EXPORTS = (
-    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_validate_bf16", "tk_plan_spans", "tk_max_k",
-    "tk_max_span_cols", "tk_status_string", "tk_build_info",
+    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
+    "tk_validate_merge_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
 )
 
 
@@ -77,6 +77,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_topk_bf16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
     lib.tk_validate_bf16.restype = i32
     lib.tk_validate_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.tk_topk_bf16_shard.restype = i32
+    lib.tk_topk_bf16_shard.argtypes = [i64, i64, i64, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.tk_merge_topk_bf16.restype = i32
+    lib.tk_merge_topk_bf16.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tk_validate_merge_bf16.restype = i32
+    lib.tk_validate_merge_bf16.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.tk_plan_spans.restype = i32
     lib.tk_plan_spans.argtypes = [i64, i64, i32, i32]
     lib.tk_max_k.restype = i32
@@ -178,3 +184,60 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
     if status != TK_OK:
         raise TkError(status, "tk_topk_bf16")
     return out
+
+
+def _outputs(torch, rows, k, device):
+    return TopK(
+        torch.empty((rows, k), dtype=torch.int32, device=device),
+        torch.empty((rows, k), dtype=torch.bfloat16, device=device),
+        torch.empty((rows,), dtype=torch.int32, device=device),
+        torch.empty((rows,), dtype=torch.int32, device=device),
+    )
+
+
+def topk_bf16_shard(x, k: int, col_base: int, *, out: TopK | None = None) -> TopK:
+    """Top-k of a column shard whose column 0 is global column ``col_base``:
+    like topk_bf16, with global indices in ``idx`` (tk_topk_bf16_shard)."""
+    import torch
+
+    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.device.type != "cuda":
+        raise ValueError("expected a 2-D bf16 tensor on a HIP device")
+    rows, cols = x.shape
+    if rows > 0 and cols > 0 and x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    out = _outputs(torch, rows, k, x.device) if out is None else out
+    status = int(load().tk_topk_bf16_shard(
+        rows, cols, x.stride(0) if rows > 1 else max(cols, 1), k, col_base, x.data_ptr(), out.idx.data_ptr(),
+        out.val.data_ptr(), out.count.data_ptr(), out.nonfinite.data_ptr(),
+        _current_stream_handle(torch, x.device.index if x.device.index is not None else torch.cuda.current_device())))
+    if status != TK_OK:
+        raise TkError(status, "tk_topk_bf16_shard")
+    return out
+
+
+def merge_topk_bf16(idx, val, count, nonfinite, *, out: TopK | None = None) -> TopK:
+    """Merges stacked shard results: idx/val [shards, rows, k], count/nonfinite
+    [shards, rows], all contiguous (tk_merge_topk_bf16)."""
+    import torch
+
+    shards, rows, k = idx.shape
+    for t in (idx, val, count, nonfinite):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("expected contiguous tensors on a HIP device")
+    if tuple(val.shape) != (shards, rows, k) or tuple(count.shape) != (shards, rows) or \
+            tuple(nonfinite.shape) != (shards, rows):
+        raise ValueError("shape mismatch between the stacked shard results")
+    out = _outputs(torch, rows, k, idx.device) if out is None else out
+    status = int(load().tk_merge_topk_bf16(
+        rows, shards, k, idx.data_ptr(), val.data_ptr(), count.data_ptr(), nonfinite.data_ptr(), out.idx.data_ptr(),
+        out.val.data_ptr(), out.count.data_ptr(), out.nonfinite.data_ptr(),
+        _current_stream_handle(torch, idx.device.index if idx.device.index is not None else torch.cuda.current_device())))
+    if status != TK_OK:
+        raise TkError(status, "tk_merge_topk_bf16")
+    return out
+
+
+def validate_merge(rows, shards, k, idx_ptr, val_ptr, count_ptr, mask_ptr, oidx, oval, ocount, omask) -> int:
+    """The host-side guards of tk_merge_topk_bf16 on raw pointers (no HIP call)."""
+    return int(load().tk_validate_merge_bf16(rows, shards, k, idx_ptr, val_ptr, count_ptr, mask_ptr, oidx, oval, ocount,
+                                             omask))

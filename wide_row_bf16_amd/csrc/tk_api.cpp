@@ -68,6 +68,40 @@ tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const voi
   return TK_OK;
 }
 
+// Guards of the shard merge: inputs [shards][rows][k] entries and
+// [shards][rows] counts and masks, outputs as tk_topk_bf16.
+tk_status guard_merge(int64_t rows, int32_t shards, int32_t k, const void *idx_in, const void *val_in,
+                      const void *count_in, const void *mask_in, const void *out_idx, const void *out_val,
+                      const void *out_count, const void *out_nonfinite) {
+  if (rows < 0 || shards < 1 || shards > TK_MAX_SHARDS) return TK_ERR_SHAPE;
+  if (k < 1 || k > kMaxK) return TK_ERR_K;
+  if (rows == 0) return TK_OK;
+  if (!idx_in || !val_in || !count_in || !mask_in || !out_idx || !out_val || !out_count || !out_nonfinite)
+    return TK_ERR_NULL;
+  const int64_t big = std::numeric_limits<int64_t>::max() / 8;
+  if (!mul_ok(rows, (int64_t)shards * k, big) || rows > (int64_t)UINT32_MAX) return TK_ERR_SHAPE;
+  if (((uintptr_t)val_in & 1) || ((uintptr_t)out_val & 1)) return TK_ERR_ALIGN;
+  if (((uintptr_t)idx_in & 3) || ((uintptr_t)count_in & 3) || ((uintptr_t)mask_in & 3) || ((uintptr_t)out_idx & 3) ||
+      ((uintptr_t)out_count & 3) || ((uintptr_t)out_nonfinite & 3))
+    return TK_ERR_ALIGN;
+  const int64_t n_in = rows * shards;
+  const Range rs[8] = {
+      {(uintptr_t)idx_in, (uintptr_t)idx_in + (uintptr_t)(4 * n_in * k)},
+      {(uintptr_t)val_in, (uintptr_t)val_in + (uintptr_t)(2 * n_in * k)},
+      {(uintptr_t)count_in, (uintptr_t)count_in + (uintptr_t)(4 * n_in)},
+      {(uintptr_t)mask_in, (uintptr_t)mask_in + (uintptr_t)(4 * n_in)},
+      {(uintptr_t)out_idx, (uintptr_t)out_idx + (uintptr_t)(4 * rows * k)},
+      {(uintptr_t)out_val, (uintptr_t)out_val + (uintptr_t)(2 * rows * k)},
+      {(uintptr_t)out_count, (uintptr_t)out_count + (uintptr_t)(4 * rows)},
+      {(uintptr_t)out_nonfinite, (uintptr_t)out_nonfinite + (uintptr_t)(4 * rows)},
+  };
+  // outputs must overlap neither each other nor any input (inputs may share memory)
+  for (int i = 4; i < 8; ++i)
+    for (int j = 0; j < 8; ++j)
+      if (j != i && overlap(rs[i], rs[j])) return TK_ERR_ALIAS;
+  return TK_OK;
+}
+
 // Smallest span count that keeps every span within one workgroup's limit.
 int64_t min_spans(int64_t cols) {
   const int64_t nv = cols / kVecElems;
@@ -193,9 +227,10 @@ void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st, b
 
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
-              const tk_options *opt) {
+              const tk_options *opt, int64_t col_base = 0) {
   tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
   if (st != TK_OK) return st;
+  if (col_base < 0 || col_base > (int64_t)INT32_MAX - cols + (cols > 0 ? 1 : 0)) return TK_ERR_SHAPE;
   int32_t forced = 0, exact = 0;
   if (opt) {
     for (int i = 0; i < 6; ++i)
@@ -226,6 +261,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   sa.out_val = out_val;
   sa.out_count = out_count;
   sa.out_nonfinite = out_nonfinite;
+  sa.col_base = col_base;
 
   const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
   if (spans == 1) {
@@ -309,6 +345,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
       m.list_in = (const uint64_t *)(base + off_list[i]);
       m.count_in = (const int32_t *)(base + off_count[i]);
       m.flags_in = (const uint32_t *)(base + off_flags[i]);
+      m.col_base = col_base;
       if (i + 1 < levels) {
         m.list_out = (uint64_t *)(base + off_list[i + 1]);
         m.count_out = (int32_t *)(base + off_count[i + 1]);
@@ -349,6 +386,40 @@ tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32
                            const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
                            const uint32_t *out_nonfinite) {
   return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite);
+}
+
+tk_status tk_topk_bf16_shard(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, int64_t col_base,
+                             const uint16_t *in, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
+                             uint32_t *out_nonfinite, void *stream) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr, col_base);
+}
+
+tk_status tk_validate_merge_bf16(int64_t rows, int32_t shards, int32_t k, const int32_t *idx_in,
+                                 const uint16_t *val_in, const int32_t *count_in, const uint32_t *mask_in,
+                                 const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
+                                 const uint32_t *out_nonfinite) {
+  return guard_merge(rows, shards, k, idx_in, val_in, count_in, mask_in, out_idx, out_val, out_count, out_nonfinite);
+}
+
+tk_status tk_merge_topk_bf16(int64_t rows, int32_t shards, int32_t k, const int32_t *idx_in, const uint16_t *val_in,
+                             const int32_t *count_in, const uint32_t *mask_in, int32_t *out_idx, uint16_t *out_val,
+                             int32_t *out_count, uint32_t *out_nonfinite, void *stream) {
+  const tk_status st =
+      guard_merge(rows, shards, k, idx_in, val_in, count_in, mask_in, out_idx, out_val, out_count, out_nonfinite);
+  if (st != TK_OK || rows == 0) return st;
+  tk::ShardMergeArgs m{};
+  m.rows = rows;
+  m.shards = shards;
+  m.k = k;
+  m.idx_in = idx_in;
+  m.val_in = val_in;
+  m.count_in = count_in;
+  m.mask_in = mask_in;
+  m.out_idx = out_idx;
+  m.out_val = out_val;
+  m.out_count = out_count;
+  m.out_nonfinite = out_nonfinite;
+  return tk::launch_shard_merge(m, (hipStream_t)stream) == hipSuccess ? TK_OK : TK_ERR_DEVICE;
 }
 
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {

@@ -675,7 +675,7 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
     const int64_t ob = r * k;
     if (l < k) {
       if (l < cnt) {
-        a.out_idx[ob + l] = col_of(acc);
+        a.out_idx[ob + l] = (int32_t)(col_of(acc) + a.col_base);
         a.out_val[ob + l] = value_bits(acc, row);
       } else {
         a.out_idx[ob + l] = TK_FILL_IDX;
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   if (S == 1) {
     const int64_t ob = r * a.k;
     if (mine && rank < a.k) {
-      a.out_idx[ob + rank] = col_of(x);
+      a.out_idx[ob + rank] = (int32_t)(col_of(x) + a.col_base);
       a.out_val[ob + rank] = value_bits(x, row);
     }
     const int t = threadIdx.x;
@@ -908,7 +908,7 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
     const int64_t ob = r * k;
     if (l < k) {
       if (l < cnt) {
-        a.out_idx[ob + l] = col_of(acc);
+        a.out_idx[ob + l] = (int32_t)(col_of(acc) + a.col_base);
         a.out_val[ob + l] = value_bits(acc, row);
       } else {
         a.out_idx[ob + l] = TK_FILL_IDX;
@@ -930,6 +930,75 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
 }
 
 }  // namespace
+
+// Merge of per-shard results (vocabulary-sharded top-k): one wave per row
+// folds the row's entry lists of all shards with the same bitonic merges.
+// Entries carry global column indices and their own bf16 bits, so the
+// composite is key << 32 | (0x7FFFFFFF - idx) << 1 | sign bit: the same (score
+// desc, index asc) order for indices below 2^31, with the sign of a zero
+// carried along (its key does not tell +0 from -0).
+__device__ __forceinline__ uint64_t shard_composite(uint32_t val, int32_t idx) {
+  return ((uint64_t)order_key(val) << 32) | ((uint64_t)(0x7FFFFFFFu - (uint32_t)idx) << 1) | ((val >> 15) & 1u);
+}
+
+__global__ __launch_bounds__(kWgThreads) void shard_merge_kernel(ShardMergeArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const int64_t r = (int64_t)blockIdx.x * kWgWaves + wave;
+  if (r >= a.rows) return;
+  const Xchg x = make_xchg();
+  const int k = a.k;
+  uint64_t acc = 0;
+  int cnt = 0;
+  uint32_t fl = 0;
+  for (int g0 = 0; g0 < a.shards; g0 += 4) {
+    uint64_t v[4];
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // four shards' loads in flight
+      const int g = g0 + j;
+      c[j] = 0;
+      v[j] = 0;
+      if (g < a.shards) {
+        const int64_t sr = (int64_t)g * a.rows + r;
+        c[j] = a.count_in[sr];
+        fl |= a.mask_in[sr];
+        if (l < c[j] && l < k) v[j] = shard_composite(a.val_in[sr * k + l], a.idx_in[sr * k + l]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (g0 + j >= a.shards) break;
+      acc = (g0 == 0 && j == 0) ? v[j] : merge_sorted64(acc, v[j], x);
+      cnt += c[j];
+    }
+  }
+  if (cnt > k) cnt = k;
+  const int64_t ob = r * k;
+  if (l < k) {
+    if (l < cnt) {
+      const uint32_t key = (uint32_t)(acc >> 32);
+      const uint32_t lo = (uint32_t)acc;
+      a.out_idx[ob + l] = (int32_t)(0x7FFFFFFFu - (lo >> 1));
+      a.out_val[ob + l] = (uint16_t)(key > 0x8000u ? key - 0x8000u
+                                                   : (key < 0x8000u ? 0x8000u | (0x8000u - key) : (lo & 1u) << 15));
+    } else {
+      a.out_idx[ob + l] = TK_FILL_IDX;
+      a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;
+    }
+  }
+  if (l == 0) {
+    a.out_count[r] = cnt;
+    a.out_nonfinite[r] = fl;
+  }
+}
+
+hipError_t launch_shard_merge(const ShardMergeArgs &a, hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  const int64_t blocks = (a.rows + kWgWaves - 1) / kWgWaves;
+  hipLaunchKernelGGL(shard_merge_kernel, dim3((uint32_t)blocks), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 __global__ void zero_fill_kernel(int32_t *p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -30,6 +30,7 @@ struct ScanArgs {
   int32_t *span_count;  // [rows][spans]
   uint32_t *span_flags; // [rows][spans]
   int32_t *row_done;    // non-NULL: fused merge; per-row arrival counters, zero between calls
+  int64_t col_base;     // added to every output column index (a shard's first global column)
 };
 
 // One merge workgroup per (row, group of up to kMergeGroup input lists).
@@ -52,7 +53,26 @@ struct MergeArgs {
   uint16_t *out_val;
   int32_t *out_count;
   uint32_t *out_nonfinite;
+  int64_t col_base;    // added to every output column index
 };
+
+// Merge of per-shard top-k results: shard g's outputs for all rows are the
+// dense blocks idx/val [g][rows][k], count/mask [g][rows].
+struct ShardMergeArgs {
+  int64_t rows;
+  int32_t shards;
+  int32_t k;
+  const int32_t *idx_in;
+  const uint16_t *val_in;
+  const int32_t *count_in;
+  const uint32_t *mask_in;
+  int32_t *out_idx;
+  uint16_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+};
+
+hipError_t launch_shard_merge(const ShardMergeArgs &a, hipStream_t stream);
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
