@@ -21,7 +21,8 @@ decision with the same numbers:
   2. x_j = the bf16 value of entry j, exactly, as float32.
      Weights: if x_0 is +inf, w_j = 1 for x_j == +inf, else 0.  Otherwise
      w_j = exp((x_j - x_0) / T), computed as
-         s  = float32(log2(e) / T)          (once per call, in float64)
+         s  = float32(log2(e) / T)          (once per call, in float64, with T
+                                             the float32 temperature as given)
          t  = float32(float32(x_j - x_0) * s)
          w  = exp2(t) by the routine exp2_f32 below; w = 0 when x_j is -inf.
   3. Cumulative sums in entry order, float32, one addition at a time:
@@ -97,7 +98,7 @@ def bf16_to_f32(bits):
 
 
 def log2e_over(temperature):
-    return F(np.float64(math.log2(math.e)) / np.float64(temperature))
+    return F(np.float64(math.log2(math.e)) / np.float64(F(temperature)))
 
 
 def sample_row(vals, count, temperature, top_p, seed, offset, row):
@@ -105,7 +106,7 @@ def sample_row(vals, count, temperature, top_p, seed, offset, row):
     row's entries in order.  The caller maps the position to a column."""
     if count <= 0:
         return -1, 0
-    if temperature == 0:
+    if F(temperature) == 0:
         return 0, 1
     x = [bf16_to_f32(vals[j]) for j in range(count)]
     if math.isinf(x[0]) and x[0] > 0:
