@@ -165,6 +165,48 @@ tk_status tk_validate_merge_bf16(int64_t rows, int32_t shards, int32_t k, const 
                                  const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
                                  const uint32_t *out_nonfinite);
 
+/*
+ * Seeded top-p sampling over the top-k entries of each row: the step a
+ * sampled drafted decode takes after top-k (the pages name its parameters,
+ * temperature, top-k, top-p and seed, in the receipt of TensorFold PR #3069
+ * "qwen27 metal: restore the long-copy driver for a lone greedy stream on
+ * M5", and require seeded sampled decodes to repeat token for token, in the
+ * seeded sampled exactness cases of the review of PR #713).  The pages give
+ * no algorithm; this is the library's reading, in float32 throughout, with
+ * every operation a single IEEE float32 operation in the order given:
+ *   inputs per row: idx/val/count as tk_topk_bf16 writes them ([rows][k],
+ *   [rows], device memory), entries in order.
+ *   - count <= 0: token -1, kept 0.  temperature == 0: greedy, token = idx[0].
+ *   - x_j = the bf16 value val[j] as float32 (exact).  If x_0 is +inf, the
+ *     weight w_j is 1 for x_j == +inf and 0 otherwise; else w_j = 0 for
+ *     x_j == -inf and w_j = exp2(float32(float32(x_j - x_0) * s)) with
+ *     s = float32(log2(e) / temperature) formed in double, and exp2 =
+ *     n = rint(t), f = t - n, 2^f by the degree-7 Taylor polynomial
+ *     (coefficients (ln 2)^i / i! as float32, Horner), times 2^n; 0 when
+ *     n < -125.
+ *   - c_0 = 0, c_{j+1} = c_j + w_j (float32, in entry order); Z = c_count.
+ *   - kept = the smallest n >= 1 with c_n >= float32(top_p * Z).
+ *   - u = (r >> 8) * 2^-24 with r the first word of Philox4x32-10 (Salmon,
+ *     Moraes, Dror and Shaw, SC 2011), key (seed low word, seed high word),
+ *     counter (row, 0, offset low word, offset high word); h =
+ *     float32(u * c_kept).
+ *   - token = idx[j] for the smallest j < kept with c_{j+1} > h, else
+ *     idx[kept - 1].
+ * Outputs: out_token, out_kept int32 [rows].  `offset` is the decode step:
+ * the same (seed, offset, row) always draws the same u.  Guards: 1 <= k <=
+ * TK_MAX_K (TK_ERR_K), 0 <= temperature finite and 0 < top_p <= 1
+ * (TK_ERR_OPTION), NULL, alignment, outputs overlapping each other or an
+ * input (TK_ERR_ALIAS).  Asynchronous on `stream`; no scratch memory.
+ */
+tk_status tk_sample_topk_bf16(int64_t rows, int32_t k, const int32_t *idx, const uint16_t *val, const int32_t *count,
+                              float temperature, float top_p, uint64_t seed, uint64_t offset, int32_t *out_token,
+                              int32_t *out_kept, void *stream);
+
+/* The host-side guards of tk_sample_topk_bf16 alone (no HIP call). */
+tk_status tk_validate_sample_bf16(int64_t rows, int32_t k, const int32_t *idx, const uint16_t *val,
+                                  const int32_t *count, float temperature, float top_p, const int32_t *out_token,
+                                  const int32_t *out_kept);
+
 int32_t tk_max_k(void);             /* == TK_MAX_K */
 int64_t tk_max_span_cols(void);     /* widest span one workgroup scans */
 const char *tk_status_string(tk_status s);

@@ -152,3 +152,19 @@ def test_shard_col_base_guard():
     assert lib.tk_topk_bf16_shard(*args, 2**31 - 100 + 1, *bufs) == SHAPE
     # rows == 0 returns before any device work; the largest valid base passes the guard
     assert lib.tk_topk_bf16_shard(0, 100, 100, 8, 2**31 - 100, *bufs) == OK
+
+
+def vs(rows=3, k=8, idx=M_IDX, val=M_VAL, cnt=M_CNT, t=0.7, p=0.95, tok=IDX, kept=CNT):
+    return tk.validate_sample(rows, k, idx, val, cnt, t, p, tok, kept)
+
+
+def test_sample_guards():
+    assert vs() == OK
+    assert vs(t=0.0) == OK and vs(p=1.0) == OK
+    assert vs(rows=0, idx=None, val=None, cnt=None, tok=None, kept=None) == OK
+    assert vs(k=0) == K and vs(k=65) == K and vs(rows=-1) == SHAPE
+    assert vs(t=-0.1) == OPTION and vs(t=float("nan")) == OPTION and vs(t=float("inf")) == OPTION
+    assert vs(p=0.0) == OPTION and vs(p=1.0001) == OPTION and vs(p=float("nan")) == OPTION
+    assert vs(val=None) == NULL and vs(kept=None) == NULL
+    assert vs(val=M_VAL + 1) == ALIGN and vs(tok=IDX + 2) == ALIGN
+    assert vs(tok=M_IDX + 16) == ALIAS and vs(kept=IDX) == ALIAS

@@ -34,7 +34,7 @@ FILL_IDX, FILL_VAL = -1, 0x7FC0
 # Every symbol the public header declares.
 EXPORTS = (
     "tk_topk_bf16", "tk_topk_bf16_ex", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
-    "tk_validate_merge_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
+    "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
 )
 
 
@@ -83,6 +83,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_merge_topk_bf16.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.tk_validate_merge_bf16.restype = i32
     lib.tk_validate_merge_bf16.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    f32, u64 = ctypes.c_float, ctypes.c_uint64
+    lib.tk_sample_topk_bf16.restype = i32
+    lib.tk_sample_topk_bf16.argtypes = [i64, i32, vp, vp, vp, f32, f32, u64, u64, vp, vp, vp]
+    lib.tk_validate_sample_bf16.restype = i32
+    lib.tk_validate_sample_bf16.argtypes = [i64, i32, vp, vp, vp, f32, f32, vp, vp]
     lib.tk_plan_spans.restype = i32
     lib.tk_plan_spans.argtypes = [i64, i64, i32, i32]
     lib.tk_max_k.restype = i32
@@ -241,3 +246,31 @@ def validate_merge(rows, shards, k, idx_ptr, val_ptr, count_ptr, mask_ptr, oidx,
     """The host-side guards of tk_merge_topk_bf16 on raw pointers (no HIP call)."""
     return int(load().tk_validate_merge_bf16(rows, shards, k, idx_ptr, val_ptr, count_ptr, mask_ptr, oidx, oval, ocount,
                                              omask))
+
+
+def sample_topk_bf16(topk: TopK, temperature: float, top_p: float, seed: int, offset: int = 0, *, out=None):
+    """Seeded top-p sampling over a top-k result (tk_sample_topk_bf16):
+    returns (token, kept), int32 [rows] each."""
+    import torch
+
+    rows, k = topk.idx.shape
+    for t in topk:
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("expected contiguous tensors on a HIP device")
+    if out is None:
+        out = (torch.empty((rows,), dtype=torch.int32, device=topk.idx.device),
+               torch.empty((rows,), dtype=torch.int32, device=topk.idx.device))
+    dev = topk.idx.device.index if topk.idx.device.index is not None else torch.cuda.current_device()
+    status = int(load().tk_sample_topk_bf16(
+        rows, k, topk.idx.data_ptr(), topk.val.data_ptr(), topk.count.data_ptr(), float(temperature), float(top_p),
+        int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), out[0].data_ptr(), out[1].data_ptr(),
+        _current_stream_handle(torch, dev)))
+    if status != TK_OK:
+        raise TkError(status, "tk_sample_topk_bf16")
+    return out
+
+
+def validate_sample(rows, k, idx_ptr, val_ptr, count_ptr, temperature, top_p, token_ptr, kept_ptr) -> int:
+    """The host-side guards of tk_sample_topk_bf16 on raw pointers (no HIP call)."""
+    return int(load().tk_validate_sample_bf16(rows, k, idx_ptr, val_ptr, count_ptr, temperature, top_p, token_ptr,
+                                              kept_ptr))

@@ -102,6 +102,32 @@ tk_status guard_merge(int64_t rows, int32_t shards, int32_t k, const void *idx_i
   return TK_OK;
 }
 
+// Guards of the sampling call: inputs [rows][k] entries and [rows] counts.
+tk_status guard_sample(int64_t rows, int32_t k, const void *idx, const void *val, const void *count, float temperature,
+                       float top_p, const void *out_token, const void *out_kept) {
+  if (rows < 0 || rows > (int64_t)UINT32_MAX) return TK_ERR_SHAPE;
+  if (k < 1 || k > kMaxK) return TK_ERR_K;
+  if (!(temperature >= 0.0f) || temperature > 3.0e38f) return TK_ERR_OPTION;  // also NaN, inf
+  if (!(top_p > 0.0f) || top_p > 1.0f) return TK_ERR_OPTION;
+  if (rows == 0) return TK_OK;
+  if (!idx || !val || !count || !out_token || !out_kept) return TK_ERR_NULL;
+  if (!mul_ok(rows, k, std::numeric_limits<int64_t>::max() / 8)) return TK_ERR_SHAPE;
+  if (((uintptr_t)val & 1) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || ((uintptr_t)out_token & 3) ||
+      ((uintptr_t)out_kept & 3))
+    return TK_ERR_ALIGN;
+  const Range rs[5] = {
+      {(uintptr_t)idx, (uintptr_t)idx + (uintptr_t)(4 * rows * k)},
+      {(uintptr_t)val, (uintptr_t)val + (uintptr_t)(2 * rows * k)},
+      {(uintptr_t)count, (uintptr_t)count + (uintptr_t)(4 * rows)},
+      {(uintptr_t)out_token, (uintptr_t)out_token + (uintptr_t)(4 * rows)},
+      {(uintptr_t)out_kept, (uintptr_t)out_kept + (uintptr_t)(4 * rows)},
+  };
+  for (int i = 3; i < 5; ++i)
+    for (int j = 0; j < 5; ++j)
+      if (j != i && overlap(rs[i], rs[j])) return TK_ERR_ALIAS;
+  return TK_OK;
+}
+
 // Smallest span count that keeps every span within one workgroup's limit.
 int64_t min_spans(int64_t cols) {
   const int64_t nv = cols / kVecElems;
@@ -420,6 +446,42 @@ tk_status tk_merge_topk_bf16(int64_t rows, int32_t shards, int32_t k, const int3
   m.out_count = out_count;
   m.out_nonfinite = out_nonfinite;
   return tk::launch_shard_merge(m, (hipStream_t)stream) == hipSuccess ? TK_OK : TK_ERR_DEVICE;
+}
+
+tk_status tk_validate_sample_bf16(int64_t rows, int32_t k, const int32_t *idx, const uint16_t *val,
+                                  const int32_t *count, float temperature, float top_p, const int32_t *out_token,
+                                  const int32_t *out_kept) {
+  return guard_sample(rows, k, idx, val, count, temperature, top_p, out_token, out_kept);
+}
+
+tk_status tk_sample_topk_bf16(int64_t rows, int32_t k, const int32_t *idx, const uint16_t *val, const int32_t *count,
+                              float temperature, float top_p, uint64_t seed, uint64_t offset, int32_t *out_token,
+                              int32_t *out_kept, void *stream) {
+  const tk_status st = guard_sample(rows, k, idx, val, count, temperature, top_p, out_token, out_kept);
+  if (st != TK_OK || rows == 0) return st;
+  tk::SampleArgs a{};
+  a.rows = rows;
+  a.k = k;
+  a.idx = idx;
+  a.val = val;
+  a.count = count;
+  a.greedy = temperature == 0.0f;
+  // log2(e) / T in double, as the float32 T was given; log2(e) from the
+  // double nearest e
+  a.scale = a.greedy ? 0.0f : (float)(std::log2(2.718281828459045) / (double)temperature);
+  a.top_p = top_p;
+  double fact = 1.0;
+  for (int i = 0; i < 8; ++i) {
+    if (i > 0) fact *= i;
+    a.coef[i] = (float)(std::pow(std::log(2.0), (double)i) / fact);
+  }
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  a.off0 = (uint32_t)offset;
+  a.off1 = (uint32_t)(offset >> 32);
+  a.out_token = out_token;
+  a.out_kept = out_kept;
+  return tk::launch_sample(a, (hipStream_t)stream) == hipSuccess ? TK_OK : TK_ERR_DEVICE;
 }
 
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {

@@ -74,6 +74,25 @@ struct ShardMergeArgs {
 
 hipError_t launch_shard_merge(const ShardMergeArgs &a, hipStream_t stream);
 
+// Seeded top-p sampling over top-k results [rows][k] (tk_sample.hip).
+struct SampleArgs {
+  int64_t rows;
+  int32_t k;
+  const int32_t *idx;
+  const uint16_t *val;
+  const int32_t *count;
+  int32_t greedy;      // temperature == 0
+  float scale;         // float32(log2(e) / temperature)
+  float top_p;
+  float coef[8];       // (ln 2)^i / i! rounded to float32
+  uint32_t key0, key1; // seed, low and high words
+  uint32_t off0, off1; // offset, low and high words
+  int32_t *out_token;
+  int32_t *out_kept;
+};
+
+hipError_t launch_sample(const SampleArgs &a, hipStream_t stream);
+
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
