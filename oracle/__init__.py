@@ -51,10 +51,15 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
             raise FileNotFoundError(path)
         build()
     lib = ctypes.CDLL(path)
-    f = lib.tko_topk_bf16
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    for name in ("tko_topk_bf16", "tko_topk_f16"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    for name in ("tko_bf16_value", "tko_f16_value"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_double
+        f.argtypes = [ctypes.c_uint16]
     _lib_cache[path] = lib
     return lib
 
@@ -71,6 +76,15 @@ def topk_bf16(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib:
 
     Returns (idx int32 [rows,k], val uint16 [rows,k], count int32 [rows], mask uint32 [rows]).
     """
+    return _topk("tko_topk_bf16", m, cols, k, threads, lib)
+
+
+def topk_f16(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib: ctypes.CDLL | None = None):
+    """The same for a matrix of IEEE fp16 bit patterns."""
+    return _topk("tko_topk_f16", m, cols, k, threads, lib)
+
+
+def _topk(fn: str, m, cols, k, threads, lib):
     m = np.ascontiguousarray(m, dtype=np.uint16)
     assert m.ndim == 2 and cols <= m.shape[1]
     rows, stride = m.shape
@@ -80,8 +94,8 @@ def topk_bf16(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib:
     cnt = np.empty(rows, dtype=np.int32)
     mask = np.empty(rows, dtype=np.uint32)
     t = default_threads() if threads is None else threads
-    rc = lib.tko_topk_bf16(rows, cols, stride, k, m.ctypes.data, idx.ctypes.data, val.ctypes.data,
-                           cnt.ctypes.data, mask.ctypes.data, t)
+    rc = getattr(lib, fn)(rows, cols, stride, k, m.ctypes.data, idx.ctypes.data, val.ctypes.data,
+                          cnt.ctypes.data, mask.ctypes.data, t)
     if rc != 0:
         raise RuntimeError(f"oracle failed (rc={rc}) rows={rows} cols={cols} stride={stride} k={k}")
     return idx, val, cnt, mask

@@ -21,6 +21,12 @@
  *     count hold index -1 and value 0x7FC0;
  *   - row_stride is in elements; columns [cols, row_stride) are never read.
  *
+ * The same for IEEE binary16 (fp16) rows, tko_topk_f16: the definition is
+ * the same, only the widening of a 16-bit pattern to its value differs (the
+ * pages' rows are bf16; fp16 logits are this library's extension, and take
+ * the same readings: NaN excluded and flagged, infinities ranked, zeros
+ * equal, padding never read).
+ *
  * Method: every value is widened exactly to double, non-NaN values are
  * collected with their column, and the list is sorted with qsort under the
  * comparison "larger value first, then smaller column first".  Because no two
@@ -46,6 +52,18 @@ static double bf16_value(uint16_t bits) {
   return (double)f;
 }
 
+/* Exact widening of an IEEE binary16 pattern: sign, 5-bit exponent (bias
+ * 15), 10-bit fraction; exponent 0 holds zeros and subnormals (fraction *
+ * 2^-24), exponent 31 infinities (fraction 0) and NaN. */
+static double f16_value(uint16_t bits) {
+  const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+  double v;
+  if (e == 31) v = f ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)f, -24);
+  else v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
 /* qsort comparator: negative when a comes first in (score desc, column asc). */
 static int score_then_lower_column(const void *pa, const void *pb) {
   const tko_entry *a = (const tko_entry *)pa;
@@ -58,6 +76,7 @@ static int score_then_lower_column(const void *pa, const void *pb) {
 }
 
 typedef struct {
+  double (*widen)(uint16_t);
   int64_t row_begin, row_end, cols, row_stride;
   int32_t k;
   const uint16_t *in;
@@ -80,7 +99,7 @@ static void *run_rows(void *arg) {
     uint32_t mask = 0;
     int64_t n = 0;
     for (int64_t c = 0; c < job->cols; ++c) {
-      double v = bf16_value(row[c]);
+      double v = job->widen(row[c]);
       if (isnan(v)) {
         mask |= 1u;
         continue;
@@ -110,16 +129,9 @@ static void *run_rows(void *arg) {
   return NULL;
 }
 
-/*
- * Row-wise top-k of a rows x cols bf16 matrix stored with row_stride elements
- * between row starts.  Outputs are dense: out_idx/out_val [rows][k],
- * out_count/out_nonfinite [rows].  Rows are split into contiguous blocks over
- * `threads` POSIX threads (threads <= 1 runs on the caller's thread).
- * Returns 0, or -1 for invalid arguments or an allocation failure.
- */
-int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
-                  int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
-                  int32_t threads) {
+static int topk_rows(double (*widen)(uint16_t), int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
+                     const uint16_t *in, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
+                     uint32_t *out_nonfinite, int32_t threads) {
   if (rows < 0 || cols < 0 || cols > INT32_MAX || row_stride < cols || k < 1) return -1;
   if (rows == 0) return 0;
   if ((cols > 0 && !in) || !out_idx || !out_val || !out_count || !out_nonfinite) return -1;
@@ -135,6 +147,7 @@ int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, con
   }
   for (int32_t t = 0; t < threads; ++t) {
     tko_job *j = &jobs[t];
+    j->widen = widen;
     j->row_begin = rows * t / threads;
     j->row_end = rows * (t + 1) / threads;
     j->cols = cols;
@@ -163,3 +176,27 @@ int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, con
   free(tids);
   return status;
 }
+
+/*
+ * Row-wise top-k of a rows x cols bf16 matrix stored with row_stride elements
+ * between row starts.  Outputs are dense: out_idx/out_val [rows][k],
+ * out_count/out_nonfinite [rows].  Rows are split into contiguous blocks over
+ * `threads` POSIX threads (threads <= 1 runs on the caller's thread).
+ * Returns 0, or -1 for invalid arguments or an allocation failure.
+ */
+int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                  int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                  int32_t threads) {
+  return topk_rows(bf16_value, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, threads);
+}
+
+/* The same for fp16 bit patterns. */
+int tko_topk_f16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                 int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                 int32_t threads) {
+  return topk_rows(f16_value, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, threads);
+}
+
+/* Exact widenings, exposed for the pins. */
+double tko_bf16_value(uint16_t bits) { return bf16_value(bits); }
+double tko_f16_value(uint16_t bits) { return f16_value(bits); }

@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     Config,
     config,
     f32_to_bf16_bits,
+    bf16_to_f16_bits,
     family_rows,
     make_config_input,
     poison_padding,

@@ -36,6 +36,22 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def bf16_to_f16_bits(m: np.ndarray) -> np.ndarray:
+    """Re-encodes a matrix of bf16 bit patterns as IEEE fp16 bit patterns:
+    numbers by round-to-nearest-even (numpy's float16 conversion; beyond the
+    fp16 range they become infinities, below it zeros of the same sign),
+    infinities as infinities, NaN as NaN of the same sign with the payload
+    moved into the fp16 fraction (the quiet bit stays the quiet bit)."""
+    b = np.ascontiguousarray(m, dtype=np.uint16)
+    f32 = (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        out = f32.astype(np.float16).view(np.uint16).copy()
+    nan = (b & 0x7FFF) > 0x7F80
+    payload = ((b & 0x7F).astype(np.uint16) << 3)
+    out[nan] = (b[nan] & 0x8000) | 0x7C00 | payload[nan]
+    return out
+
+
 def poison_padding(m: np.ndarray, cols: int) -> np.ndarray:
     """Fill columns [cols, stride) of every row with alternating +inf / NaN bits."""
     pad = m.shape[1] - cols
@@ -330,9 +346,21 @@ FAMILIES = {
 }
 
 
-def family_rows(name: str, rows: int, cols: int, stride: int | None = None, seed: int = 0) -> np.ndarray:
-    """A (rows, stride) matrix of the named family, poison in the padding."""
+def family_rows(name: str, rows: int, cols: int, stride: int | None = None, seed: int = 0,
+                fmt: str = "bf16") -> np.ndarray:
+    """A (rows, stride) matrix of the named family, poison in the padding.
+    fmt "f16" re-encodes the family's values as fp16 bit patterns
+    (bf16_to_f16_bits); the uniform_bits family keeps its raw random
+    patterns, which cover every fp16 class as they cover every bf16 class."""
     stride = cols if stride is None else stride
     rng = np.random.default_rng(seed)
     body = FAMILIES[name](rng, rows, cols) if cols > 0 else np.empty((rows, 0), dtype=np.uint16)
-    return _strided(rows, cols, stride, body.astype(np.uint16))
+    body = body.astype(np.uint16)
+    if fmt == "f16" and name != "uniform_bits":
+        body = bf16_to_f16_bits(body)
+    elif fmt not in ("bf16", "f16"):
+        raise ValueError(f"unknown format {fmt}")
+    m = _strided(rows, cols, stride, body)
+    if fmt == "f16" and stride > cols:
+        m[:, cols:] = bf16_to_f16_bits(m[:, cols:])  # poison stays poison: +inf and NaN patterns
+    return m

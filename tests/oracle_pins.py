@@ -56,16 +56,16 @@ def widen(bits: np.ndarray) -> np.ndarray:
         return f32.astype(np.float64)
 
 
-def expected_mask(bits: np.ndarray) -> np.ndarray:
-    v = widen(bits)
+def expected_mask(bits: np.ndarray, widen_fn=None) -> np.ndarray:
+    v = (widen_fn or widen)(bits)
     return (np.isnan(v).any(axis=-1) * 1 | (v == np.inf).any(axis=-1) * 2 | (v == -np.inf).any(axis=-1) * 4).astype(np.uint32)
 
 
-def rank_definition(bits: np.ndarray, k: int):
+def rank_definition(bits: np.ndarray, k: int, widen_fn=None):
     """Top-k of each row of an (n, L) uint16 matrix by counting ranks (O(L^2) per row)."""
     bits = np.asarray(bits, dtype=np.uint16)
     n, L = bits.shape
-    v = widen(bits)
+    v = (widen_fn or widen)(bits)
     nan = np.isnan(v)
     vi = v[:, :, None]
     vj = v[:, None, :]
@@ -83,42 +83,42 @@ def rank_definition(bits: np.ndarray, k: int):
         idx[has, j] = where[has]
         val[has, j] = bits[rows[has], where[has]]
     count = np.minimum(k, (~nan).sum(axis=1)).astype(np.int32)
-    return idx, val, count, expected_mask(bits)
+    return idx, val, count, expected_mask(bits, widen_fn)
 
 
-def lexsort_reference(row: np.ndarray, k: int):
-    v = widen(row)
+def lexsort_reference(row: np.ndarray, k: int, widen_fn=None):
+    v = (widen_fn or widen)(row)
     keep = np.nonzero(~np.isnan(v))[0]
     order = keep[np.lexsort((keep, -v[keep]))]
-    return _pack(row, order, k)
+    return _pack(row, order, k, widen_fn)
 
 
-def python_sorted_reference(row: np.ndarray, k: int):
-    v = widen(row).tolist()
+def python_sorted_reference(row: np.ndarray, k: int, widen_fn=None):
+    v = (widen_fn or widen)(row).tolist()
     order = sorted((c for c in range(len(v)) if v[c] == v[c]), key=lambda c: (-v[c], c))
-    return _pack(row, np.array(order, dtype=np.int64), k)
+    return _pack(row, np.array(order, dtype=np.int64), k, widen_fn)
 
 
-def _pack(row, order, k):
+def _pack(row, order, k, widen_fn=None):
     count = min(k, len(order))
     idx = np.full(k, -1, dtype=np.int32)
     val = np.full(k, 0x7FC0, dtype=np.uint16)
     idx[:count] = order[:count]
     val[:count] = row[order[:count]]
-    return idx, val, count, int(expected_mask(row[None])[0])
+    return idx, val, count, int(expected_mask(row[None], widen_fn)[0])
 
 
 def run(lib, m, cols, k, threads=1):
     return oracle.topk_bf16(m, cols, k, threads=threads, lib=lib)
 
 
-def check_invariants(m: np.ndarray, cols: int, k: int, idx, val, cnt, mask):
+def check_invariants(m: np.ndarray, cols: int, k: int, idx, val, cnt, mask, widen_fn=None):
     """Properties that hold for any correct answer, at any size."""
     body = m[:, :cols]
-    v = widen(body)
+    v = (widen_fn or widen)(body)
     nan = np.isnan(v)
     assert np.array_equal(cnt, np.minimum(k, (~nan).sum(axis=1)))
-    assert np.array_equal(mask, expected_mask(body))
+    assert np.array_equal(mask, expected_mask(body, widen_fn))
     for r in range(m.shape[0]):
         c = int(cnt[r])
         e = idx[r, :c].astype(np.int64)
