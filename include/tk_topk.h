@@ -107,6 +107,20 @@ tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_
                           void *stream, const tk_options *opt);
 
 /*
+ * IEEE binary16 (fp16) rows: the same operation, layouts, outputs, guards
+ * and options as tk_topk_bf16 / tk_topk_bf16_ex, with `in` holding fp16 bit
+ * patterns (+inf 0x7C00, -inf 0xFC00, NaN any magnitude above 0x7C00).  The
+ * pages' rows are bf16; fp16 logits are an extension on the same row ABI.
+ * out_val holds the fp16 bits of the entries; empty slots hold 0x7FC0 (an
+ * fp16 NaN pattern too).  tk_validate_bf16 gives the guards of both.
+ */
+tk_status tk_topk_f16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                      int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream);
+tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                         int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                         void *stream, const tk_options *opt);
+
+/*
  * The host-side guards alone (no HIP call is made): returns the status
  * tk_topk_bf16 would return before launching anything.
  */

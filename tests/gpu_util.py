@@ -52,11 +52,13 @@ def to_numpy(out):
     )
 
 
-def gpu_topk(m: np.ndarray, cols: int, k: int, spans: int = 0, offset: int = 0, x=None):
+def gpu_topk(m: np.ndarray, cols: int, k: int, spans: int = 0, offset: int = 0, x=None, fmt: str = "bf16",
+             exact: bool = False):
     import wide_row_bf16_amd as tk
 
     x = upload(m, offset) if x is None else x
-    return to_numpy(tk.topk_bf16(x, k, cols=cols, spans=spans))
+    fn = tk.topk_bf16 if fmt == "bf16" else tk.topk_f16
+    return to_numpy(fn(x, k, cols=cols, spans=spans, exact=exact))
 
 
 def assert_same(got, want, what: str):
@@ -70,8 +72,9 @@ def assert_same(got, want, what: str):
             )
 
 
-def check_case(m, cols, k, spans=0, offset=0, what="", want=None):
-    want = oracle.topk_bf16(m, cols, k) if want is None else want
-    got = gpu_topk(m, cols, k, spans=spans, offset=offset)
+def check_case(m, cols, k, spans=0, offset=0, what="", want=None, fmt="bf16"):
+    if want is None:
+        want = (oracle.topk_bf16 if fmt == "bf16" else oracle.topk_f16)(m, cols, k)
+    got = gpu_topk(m, cols, k, spans=spans, offset=offset, fmt=fmt)
     assert_same(got, want, what or f"cols={cols} k={k} spans={spans} offset={offset}")
     return got

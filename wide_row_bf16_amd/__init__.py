@@ -33,7 +33,7 @@ FILL_IDX, FILL_VAL = -1, 0x7FC0
 
 # Every symbol the public header declares.
 EXPORTS = (
-    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
+    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_topk_f16", "tk_topk_f16_ex", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
     "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
 )
 
@@ -75,6 +75,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_topk_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.tk_topk_bf16_ex.restype = i32
     lib.tk_topk_bf16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
+    lib.tk_topk_f16.restype = i32
+    lib.tk_topk_f16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.tk_topk_f16_ex.restype = i32
+    lib.tk_topk_f16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
     lib.tk_validate_bf16.restype = i32
     lib.tk_validate_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.tk_topk_bf16_shard.restype = i32
@@ -128,14 +132,16 @@ def validate(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mas
 
 
 def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream=0, spans=0,
-                  exact=0) -> int:
-    """Calls the C ABI on raw device pointers; returns the status code."""
+                  exact=0, fmt="bf16") -> int:
+    """Calls the C ABI on raw device pointers (fmt "bf16" or "f16"); returns
+    the status code."""
     lib = load()
+    name = {"bf16": "tk_topk_bf16", "f16": "tk_topk_f16"}[fmt]
     if spans or exact:
         opt = TkOptions(spans=spans, exact=exact)
-        return int(lib.tk_topk_bf16_ex(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
-                                       stream, ctypes.byref(opt)))
-    return int(lib.tk_topk_bf16(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
+        return int(getattr(lib, name + "_ex")(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
+                                              stream, ctypes.byref(opt)))
+    return int(getattr(lib, name)(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
 
 
 def _current_stream_handle(torch, dev: int) -> int:
@@ -146,7 +152,7 @@ def _current_stream_handle(torch, dev: int) -> int:
 
 
 def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool = False, out: TopK | None = None,
-              stream=None) -> TopK:
+              stream=None, _fmt: str = "bf16") -> TopK:
     """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
 
     ``cols`` limits the scan to the first ``cols`` columns (default: all);
@@ -159,8 +165,9 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
 
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError(f"expected bf16 bit patterns, got {x.dtype}")
+    wanted = torch.bfloat16 if _fmt == "bf16" else torch.float16
+    if x.dtype not in (wanted, torch.int16, torch.uint16):
+        raise TypeError(f"expected {_fmt} bit patterns, got {x.dtype}")
     if x.device.type != "cuda":
         raise ValueError("expected a tensor on a HIP device")
     rows, width = x.shape
@@ -173,22 +180,27 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
     if out is None:
         out = TopK(
             torch.empty((rows, k), dtype=torch.int32, device=x.device),
-            torch.empty((rows, k), dtype=torch.bfloat16, device=x.device),
+            torch.empty((rows, k), dtype=wanted, device=x.device),
             torch.empty((rows,), dtype=torch.int32, device=x.device),
             torch.empty((rows,), dtype=torch.int32, device=x.device),
         )
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
     args = (rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
-            out.nonfinite.data_ptr(), handle, spans, int(exact))
+            out.nonfinite.data_ptr(), handle, spans, int(exact), _fmt)
     if dev == torch.cuda.current_device():
         status = topk_bf16_raw(*args)
     else:
         with torch.cuda.device(dev):
             status = topk_bf16_raw(*args)
     if status != TK_OK:
-        raise TkError(status, "tk_topk_bf16")
+        raise TkError(status, "tk_topk_" + _fmt)
     return out
+
+
+def topk_f16(x, k: int, **kw) -> TopK:
+    """topk_bf16 for IEEE fp16 rows (tk_topk_f16); ``val`` holds fp16 bits."""
+    return topk_bf16(x, k, _fmt="f16", **kw)
 
 
 def _outputs(torch, rows, k, device):

@@ -253,7 +253,7 @@ void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st, b
 
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
-              const tk_options *opt, int64_t col_base = 0) {
+              const tk_options *opt, int64_t col_base = 0, uint32_t inf = 0x7F80u) {
   tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
   if (st != TK_OK) return st;
   if (col_base < 0 || col_base > (int64_t)INT32_MAX - cols + (cols > 0 ? 1 : 0)) return TK_ERR_SHAPE;
@@ -288,6 +288,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   sa.out_count = out_count;
   sa.out_nonfinite = out_nonfinite;
   sa.col_base = col_base;
+  sa.inf = inf;
 
   const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
   if (spans == 1) {
@@ -406,6 +407,17 @@ tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_
                           int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                           void *stream, const tk_options *opt) {
   return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, opt);
+}
+
+tk_status tk_topk_f16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                      int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr, 0, 0x7C00u);
+}
+
+tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                         int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                         void *stream, const tk_options *opt) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, opt, 0, 0x7C00u);
 }
 
 tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,

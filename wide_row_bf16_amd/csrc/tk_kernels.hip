@@ -11,7 +11,10 @@
 // 16-bit key 0x8000 + m (sign clear) or 0x8000 - m (sign set).  The key is
 // monotone in value, gives +0 and -0 the same key 0x8000, keeps subnormals
 // in order, and sends -inf to 0x0080 and +inf to 0xFF80.  NaN (m > 0x7F80)
-// gets key 0, below every number, and is never kept.  Inside one wave the
+// gets key 0, below every number, and is never kept.  IEEE fp16 patterns are
+// sign-magnitude too: the same map works with +inf at 0x7C00 (keys 0x0400
+// and 0xFC00 for -inf and +inf), so the scan takes the +inf pattern as an
+// argument.  Inside one wave the
 // composite (key << 16) | (0xFFFF - rel), rel = column - wave base < 65536,
 // is a strict total order equal to (score desc, column asc); across waves and
 // spans the 64-bit composite (key << 32) | (0xFFFFFFFF - column) is used.
@@ -51,7 +54,7 @@ typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kNan = TK_NONFINITE_NAN;
 constexpr uint32_t kPinf = TK_NONFINITE_POSINF;
 constexpr uint32_t kNinf = TK_NONFINITE_NEGINF;
-constexpr uint32_t kKeyPosInf = 0xFF80u;
+constexpr uint32_t kBf16Inf = 0x7F80u;  // bf16 +inf pattern (fp16: 0x7C00, passed at run time)
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
@@ -236,10 +239,12 @@ __device__ __forceinline__ void sort8_desc(uint32_t (&c)[8]) {
   cx(c[1], c[2]); cx(c[3], c[4]); cx(c[5], c[6]);
 }
 
-__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+// inf = the format's +inf pattern (bf16 0x7F80, fp16 0x7C00): magnitudes
+// above it are NaN.
+__device__ __forceinline__ uint32_t order_key(uint32_t b, uint32_t inf = kBf16Inf) {
   const uint32_t mag = b & 0x7FFFu;
   const uint32_t key = (b & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
-  return mag > 0x7F80u ? 0u : key;
+  return mag > inf ? 0u : key;
 }
 
 struct WaveTopK {
@@ -248,6 +253,7 @@ struct WaveTopK {
   uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of other waves
   uint32_t floor;  // wave-uniform floor: only keys > floor are kept (0 = none)
   uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
+  uint32_t inf;    // wave-uniform +inf pattern of the input format
   int km1;         // k - 1
   int qm1;         // ceil(k / 4) - 1
   int wave;        // this wave's index in the workgroup
@@ -323,7 +329,8 @@ __device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
   f.nonneg = tkey >= 0x8000u;
   f.t16 = (int32_t)tkey - 0x8000;
   f.tu = 0x10000u - tkey;
-  f.ftrip = (flags & kNinf) ? ((flags & kNan) ? 0x10000u : 0xFF81u) : 0xFF80u;
+  const uint32_t ninf = 0x8000u | (uint32_t)__builtin_amdgcn_readfirstlane((int)w.inf);
+  f.ftrip = (flags & kNinf) ? ((flags & kNan) ? 0x10000u : ninf + 1u) : ninf;
   return f;
 }
 
@@ -369,9 +376,9 @@ __device__ __forceinline__ void take_vector_dense(WaveTopK &w, uint4 d, uint32_t
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-    const uint32_t key = order_key(b);
-    nan |= (b & 0x7FFFu) > 0x7F80u;
-    ninf |= b == 0xFF80u;
+    const uint32_t key = order_key(b, w.inf);
+    nan |= (b & 0x7FFFu) > w.inf;
+    ninf |= b == (0x8000u | w.inf);
     c[e] = (valid && key > w.ext) ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
   }
   if (ballot(valid && nan)) w.flags |= kNan;
@@ -410,7 +417,7 @@ __device__ __forceinline__ void take_lanes_value(WaveTopK &w, uint4 d, uint32_t 
     if (!m[e]) continue;
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
-    const uint32_t key = NONNEG ? (b > 0x7F80u ? 0u : b | 0x8000u) : order_key(b);
+    const uint32_t key = NONNEG ? (b > w.inf ? 0u : b | 0x8000u) : order_key(b, w.inf);
     if (m[e] & lanes_eq(key, 0u)) w.flags |= kNan;
     const uint32_t c = key ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
     uint64_t h = m[e] & lanes_ugt(c, w.kth);
@@ -432,8 +439,8 @@ __device__ __forceinline__ void take_flags(WaveTopK &w, uint4 d, uint64_t lanes,
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
     const uint64_t m = lanes_uge(b, ftrip) & lanes;
-    if (m & lanes_eq(b, 0xFF80u)) w.flags |= kNinf;
-    if (m & lanes_ugt(b, 0xFF80u)) w.flags |= kNan;
+    if (m & lanes_eq(b, 0x8000u | w.inf)) w.flags |= kNinf;
+    if (m & lanes_ugt(b, 0x8000u | w.inf)) w.flags |= kNan;
   }
 }
 
@@ -445,9 +452,9 @@ __device__ void take_columns(WaveTopK &w, const uint16_t *row, int64_t lo, int64
     const int64_t col = c0 + lane_id();
     const bool valid = col < hi;
     const uint32_t b = valid ? (uint32_t)row[col] : 0u;
-    const uint32_t key = order_key(b);
-    if (ballot(valid && (b & 0x7FFFu) > 0x7F80u)) w.flags |= kNan;
-    if (ballot(valid && b == 0xFF80u)) w.flags |= kNinf;
+    const uint32_t key = order_key(b, w.inf);
+    if (ballot(valid && (b & 0x7FFFu) > w.inf)) w.flags |= kNan;
+    if (ballot(valid && b == (0x8000u | w.inf))) w.flags |= kNinf;
     const uint32_t c = (valid && key > w.ext) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
     const uint64_t m = lanes_ugt(c, w.kth);
     if (m) offer(w, c, m);
@@ -542,14 +549,15 @@ __device__ __forceinline__ void load_chunk(uint4 (&dst)[kChunkVecs], const uint4
 // This lane's largest order key in a loaded chunk (vectors [first, first +
 // kChunkVecs * 64) of nvec; vectors at or past nvec count as key 0, as does
 // NaN).  Sorted over the wave, these give the floors of span_scan_kernel.
-__device__ __forceinline__ uint32_t lane_max_key(const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec) {
+__device__ __forceinline__ uint32_t lane_max_key(const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
+                                                 uint32_t inf) {
   uint32_t m = 0;
 #pragma unroll
   for (int u = 0; u < kChunkVecs; ++u) {
     const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     uint32_t mu = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mu = max(mu, order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+    for (int e = 0; e < 8; ++e) mu = max(mu, order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu, inf));
     if (first + (uint32_t)(u * kWave + lane_id()) < nvec) m = max(m, mu);
   }
   return m;
@@ -748,7 +756,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
       a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
   {
     const Xchg x = make_xchg();
-    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn) : 0u, x);
+    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn, a.inf) : 0u, x);
     __syncthreads();
     const uint32_t m01 = bitonic_merge64_desc(max(s_samp[0][l], partner<63>(s_samp[1][l], x)), x);
     const uint32_t m23 = bitonic_merge64_desc(max(s_samp[2][l], partner<63>(s_samp[3][l], x)), x);
@@ -776,6 +784,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     w.ext = floor;
     w.floor = floor;
     w.flags = 0;
+    w.inf = a.inf;
     w.km1 = a.k - 1;
     w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
     w.wave = wave;
@@ -792,7 +801,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     if (l == 0) {
       const int cnt = __popcll(valid_mask);
       s_count[wave] = cnt < a.k ? cnt : a.k;
-      s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == kKeyPosInf ? kPinf : 0u);
+      s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == 0x8000u + a.inf ? kPinf : 0u);
     }
     __syncthreads();
 

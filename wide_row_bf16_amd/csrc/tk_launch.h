@@ -31,6 +31,7 @@ struct ScanArgs {
   uint32_t *span_flags; // [rows][spans]
   int32_t *row_done;    // non-NULL: fused merge; per-row arrival counters, zero between calls
   int64_t col_base;     // added to every output column index (a shard's first global column)
+  uint32_t inf;         // +inf bit pattern of the input format: 0x7F80 bf16, 0x7C00 fp16
 };
 
 // One merge workgroup per (row, group of up to kMergeGroup input lists).
