@@ -56,6 +56,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    f = lib.tko_topk_f32
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
     for name in ("tko_bf16_value", "tko_f16_value"):
         f = getattr(lib, name)
         f.restype = ctypes.c_double
@@ -82,6 +86,27 @@ def topk_bf16(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib:
 def topk_f16(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib: ctypes.CDLL | None = None):
     """The same for a matrix of IEEE fp16 bit patterns."""
     return _topk("tko_topk_f16", m, cols, k, threads, lib)
+
+
+def topk_f32(m: np.ndarray, cols: int, k: int, threads: int | None = None, lib: ctypes.CDLL | None = None):
+    """Top-k of every row of a (rows, stride) uint32 matrix of fp32 bit patterns.
+
+    Returns (idx int32 [rows,k], val uint32 [rows,k] fp32 bits, count int32 [rows], mask uint32 [rows]).
+    """
+    m = np.ascontiguousarray(m, dtype=np.uint32)
+    assert m.ndim == 2 and cols <= m.shape[1]
+    rows, stride = m.shape
+    lib = lib or load()
+    idx = np.empty((rows, k), dtype=np.int32)
+    val = np.empty((rows, k), dtype=np.uint32)
+    cnt = np.empty(rows, dtype=np.int32)
+    mask = np.empty(rows, dtype=np.uint32)
+    t = default_threads() if threads is None else threads
+    rc = lib.tko_topk_f32(rows, cols, stride, k, m.ctypes.data, idx.ctypes.data, val.ctypes.data, cnt.ctypes.data,
+                          mask.ctypes.data, t)
+    if rc != 0:
+        raise RuntimeError(f"oracle failed (rc={rc}) rows={rows} cols={cols} stride={stride} k={k}")
+    return idx, val, cnt, mask
 
 
 def _topk(fn: str, m, cols, k, threads, lib):

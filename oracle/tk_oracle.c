@@ -21,6 +21,10 @@
  *     count hold index -1 and value 0x7FC0;
  *   - row_stride is in elements; columns [cols, row_stride) are never read.
  *
+ * The same for IEEE binary32 (fp32) rows, tko_topk_f32, with 32-bit inputs,
+ * 32-bit entry values (the input's own bits) and the fill value 0x7FC00000
+ * (a quiet fp32 NaN).
+ *
  * The same for IEEE binary16 (fp16) rows, tko_topk_f16: the definition is
  * the same, only the widening of a 16-bit pattern to its value differs (the
  * pages' rows are bf16; fp16 logits are this library's extension, and take
@@ -45,8 +49,8 @@ typedef struct {
 } tko_entry;
 
 /* Exact widening of a bf16 bit pattern: bf16 is the top half of a binary32. */
-static double bf16_value(uint16_t bits) {
-  uint32_t u = (uint32_t)bits << 16;
+static double bf16_value(uint32_t bits) {
+  uint32_t u = (bits & 0xFFFFu) << 16;
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
@@ -55,13 +59,20 @@ static double bf16_value(uint16_t bits) {
 /* Exact widening of an IEEE binary16 pattern: sign, 5-bit exponent (bias
  * 15), 10-bit fraction; exponent 0 holds zeros and subnormals (fraction *
  * 2^-24), exponent 31 infinities (fraction 0) and NaN. */
-static double f16_value(uint16_t bits) {
-  const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+static double f16_value(uint32_t bits) {
+  const int sign = (bits >> 15) & 1, e = (bits >> 10) & 31, f = bits & 1023;
   double v;
   if (e == 31) v = f ? NAN : INFINITY;
   else if (e == 0) v = ldexp((double)f, -24);
   else v = ldexp((double)(1024 + f), e - 25);
   return sign ? -v : v;
+}
+
+/* Exact widening of an IEEE binary32 pattern. */
+static double f32_value(uint32_t bits) {
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
 }
 
 /* qsort comparator: negative when a comes first in (score desc, column asc). */
@@ -76,16 +87,27 @@ static int score_then_lower_column(const void *pa, const void *pb) {
 }
 
 typedef struct {
-  double (*widen)(uint16_t);
+  double (*widen)(uint32_t);  /* exact value of one input word */
+  int word;                   /* bytes per input and entry value: 2 or 4 */
+  uint32_t fill;              /* entry value of empty slots */
   int64_t row_begin, row_end, cols, row_stride;
   int32_t k;
-  const uint16_t *in;
+  const void *in;
   int32_t *out_idx;
-  uint16_t *out_val;
+  void *out_val;
   int32_t *out_count;
   uint32_t *out_nonfinite;
   int status;
 } tko_job;
+
+static uint32_t word_at(const void *base, int64_t i, int word) {
+  return word == 2 ? ((const uint16_t *)base)[i] : ((const uint32_t *)base)[i];
+}
+
+static void put_word(void *base, int64_t i, uint32_t v, int word) {
+  if (word == 2) ((uint16_t *)base)[i] = (uint16_t)v;
+  else ((uint32_t *)base)[i] = v;
+}
 
 static void *run_rows(void *arg) {
   tko_job *job = (tko_job *)arg;
@@ -95,11 +117,11 @@ static void *run_rows(void *arg) {
     return NULL;
   }
   for (int64_t r = job->row_begin; r < job->row_end; ++r) {
-    const uint16_t *row = job->in + r * job->row_stride;
+    const int64_t row = r * job->row_stride;
     uint32_t mask = 0;
     int64_t n = 0;
     for (int64_t c = 0; c < job->cols; ++c) {
-      double v = job->widen(row[c]);
+      double v = job->widen(word_at(job->in, row + c, job->word));
       if (isnan(v)) {
         mask |= 1u;
         continue;
@@ -115,10 +137,10 @@ static void *run_rows(void *arg) {
       int64_t o = r * job->k + j;
       if (j < count) {
         job->out_idx[o] = list[j].col;
-        job->out_val[o] = row[list[j].col];
+        put_word(job->out_val, o, word_at(job->in, row + list[j].col, job->word), job->word);
       } else {
         job->out_idx[o] = -1;
-        job->out_val[o] = 0x7FC0;
+        put_word(job->out_val, o, job->fill, job->word);
       }
     }
     job->out_count[r] = (int32_t)count;
@@ -129,9 +151,9 @@ static void *run_rows(void *arg) {
   return NULL;
 }
 
-static int topk_rows(double (*widen)(uint16_t), int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
-                     const uint16_t *in, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
-                     uint32_t *out_nonfinite, int32_t threads) {
+static int topk_rows(double (*widen)(uint32_t), int word, uint32_t fill, int64_t rows, int64_t cols,
+                     int64_t row_stride, int32_t k, const void *in, int32_t *out_idx, void *out_val,
+                     int32_t *out_count, uint32_t *out_nonfinite, int32_t threads) {
   if (rows < 0 || cols < 0 || cols > INT32_MAX || row_stride < cols || k < 1) return -1;
   if (rows == 0) return 0;
   if ((cols > 0 && !in) || !out_idx || !out_val || !out_count || !out_nonfinite) return -1;
@@ -148,6 +170,8 @@ static int topk_rows(double (*widen)(uint16_t), int64_t rows, int64_t cols, int6
   for (int32_t t = 0; t < threads; ++t) {
     tko_job *j = &jobs[t];
     j->widen = widen;
+    j->word = word;
+    j->fill = fill;
     j->row_begin = rows * t / threads;
     j->row_end = rows * (t + 1) / threads;
     j->cols = cols;
@@ -187,16 +211,27 @@ static int topk_rows(double (*widen)(uint16_t), int64_t rows, int64_t cols, int6
 int tko_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
                   int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                   int32_t threads) {
-  return topk_rows(bf16_value, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, threads);
+  return topk_rows(bf16_value, 2, 0x7FC0u, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite,
+                   threads);
 }
 
 /* The same for fp16 bit patterns. */
 int tko_topk_f16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
                  int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                  int32_t threads) {
-  return topk_rows(f16_value, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, threads);
+  return topk_rows(f16_value, 2, 0x7FC0u, rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite,
+                   threads);
+}
+
+/* The same for fp32 bit patterns: 32-bit entry values, fill 0x7FC00000. */
+int tko_topk_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                 int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                 int32_t threads) {
+  return topk_rows(f32_value, 4, 0x7FC00000u, rows, cols, row_stride, k, in, out_idx, out_val, out_count,
+                   out_nonfinite, threads);
 }
 
 /* Exact widenings, exposed for the pins. */
 double tko_bf16_value(uint16_t bits) { return bf16_value(bits); }
 double tko_f16_value(uint16_t bits) { return f16_value(bits); }
+

@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     config,
     f32_to_bf16_bits,
     bf16_to_f16_bits,
+    bf16_to_f32_bits,
     family_rows,
     make_config_input,
     poison_padding,

@@ -346,16 +346,50 @@ FAMILIES = {
 }
 
 
+# Families whose values are continuous draws: their fp32 form gets random low
+# fraction bits (breaking the ties the bf16 grid creates); the others keep
+# their exact ties, zeros and special patterns.
+F32_JITTER = ("normal", "logit", "nan_sprinkled", "posinf_few", "mixed_nonfinite", "ascending", "descending")
+
+
+def bf16_to_f32_bits(m: np.ndarray, rng: np.random.Generator | None = None) -> np.ndarray:
+    """fp32 bit patterns holding the bf16 patterns' values exactly (bits <<
+    16); with rng, finite nonzero values get random low 16 fraction bits (the
+    exponent, and so the class, is unchanged)."""
+    b = np.ascontiguousarray(m, dtype=np.uint16)
+    out = b.astype(np.uint32) << np.uint32(16)
+    if rng is not None:
+        finite = (b & 0x7FFF) < 0x7F80
+        nonzero = (b & 0x7FFF) != 0
+        jitter = rng.integers(0, 1 << 16, size=b.shape, dtype=np.uint32)
+        out = np.where(finite & nonzero, out | jitter, out).astype(np.uint32)
+    return out
+
+
 def family_rows(name: str, rows: int, cols: int, stride: int | None = None, seed: int = 0,
                 fmt: str = "bf16") -> np.ndarray:
     """A (rows, stride) matrix of the named family, poison in the padding.
     fmt "f16" re-encodes the family's values as fp16 bit patterns
     (bf16_to_f16_bits); the uniform_bits family keeps its raw random
-    patterns, which cover every fp16 class as they cover every bf16 class."""
+    patterns, which cover every fp16 class as they cover every bf16 class.
+    fmt "f32" returns a uint32 matrix of fp32 patterns (bf16_to_f32_bits,
+    with low fraction bits drawn for the continuous families; uniform_bits
+    draws all 32 bits)."""
     stride = cols if stride is None else stride
     rng = np.random.default_rng(seed)
     body = FAMILIES[name](rng, rows, cols) if cols > 0 else np.empty((rows, 0), dtype=np.uint16)
     body = body.astype(np.uint16)
+    if fmt == "f32":
+        if name == "uniform_bits":
+            hi = body.astype(np.uint32) << np.uint32(16)
+            body32 = hi | rng.integers(0, 1 << 16, size=body.shape, dtype=np.uint32)
+        else:
+            body32 = bf16_to_f32_bits(body, rng if name in F32_JITTER else None)
+        m = np.empty((rows, stride), dtype=np.uint32)
+        m[:, :cols] = body32
+        if stride > cols:
+            m[:, cols:] = bf16_to_f32_bits(_strided(rows, cols, stride, body)[:, cols:])  # +inf / NaN poison
+        return m
     if fmt == "f16" and name != "uniform_bits":
         body = bf16_to_f16_bits(body)
     elif fmt not in ("bf16", "f16"):

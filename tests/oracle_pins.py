@@ -61,9 +61,10 @@ def expected_mask(bits: np.ndarray, widen_fn=None) -> np.ndarray:
     return (np.isnan(v).any(axis=-1) * 1 | (v == np.inf).any(axis=-1) * 2 | (v == -np.inf).any(axis=-1) * 4).astype(np.uint32)
 
 
-def rank_definition(bits: np.ndarray, k: int, widen_fn=None):
-    """Top-k of each row of an (n, L) uint16 matrix by counting ranks (O(L^2) per row)."""
-    bits = np.asarray(bits, dtype=np.uint16)
+def rank_definition(bits: np.ndarray, k: int, widen_fn=None, word=np.uint16, fill=0x7FC0):
+    """Top-k of each row of an (n, L) matrix of bit patterns (uint16, or
+    uint32 with word/fill for fp32) by counting ranks (O(L^2) per row)."""
+    bits = np.asarray(bits, dtype=word)
     n, L = bits.shape
     v = (widen_fn or widen)(bits)
     nan = np.isnan(v)
@@ -74,7 +75,7 @@ def rank_definition(bits: np.ndarray, k: int, widen_fn=None):
     rank = beats.sum(axis=2)
     rank[nan] = L + 1
     idx = np.full((n, k), -1, dtype=np.int32)
-    val = np.full((n, k), 0x7FC0, dtype=np.uint16)
+    val = np.full((n, k), fill, dtype=word)
     rows = np.arange(n)
     for j in range(min(k, L)):
         hit = rank == j
@@ -112,7 +113,7 @@ def run(lib, m, cols, k, threads=1):
     return oracle.topk_bf16(m, cols, k, threads=threads, lib=lib)
 
 
-def check_invariants(m: np.ndarray, cols: int, k: int, idx, val, cnt, mask, widen_fn=None):
+def check_invariants(m: np.ndarray, cols: int, k: int, idx, val, cnt, mask, widen_fn=None, fill=0x7FC0):
     """Properties that hold for any correct answer, at any size."""
     body = m[:, :cols]
     v = (widen_fn or widen)(body)
@@ -122,7 +123,7 @@ def check_invariants(m: np.ndarray, cols: int, k: int, idx, val, cnt, mask, wide
     for r in range(m.shape[0]):
         c = int(cnt[r])
         e = idx[r, :c].astype(np.int64)
-        assert np.all(idx[r, c:] == -1) and np.all(val[r, c:] == 0x7FC0)
+        assert np.all(idx[r, c:] == -1) and np.all(val[r, c:] == fill)
         assert np.all((e >= 0) & (e < cols))
         assert len(np.unique(e)) == c
         assert np.array_equal(val[r, :c], body[r, e])  # bits copied verbatim

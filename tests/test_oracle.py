@@ -71,18 +71,20 @@ MUTANTS = {
     "ties_to_higher_index": ("if (a->col < b->col) return -1;\n  if (a->col > b->col) return 1;",
                              "if (a->col > b->col) return -1;\n  if (a->col < b->col) return 1;"),
     "nan_kept": ("mask |= 1u;\n        continue;", "mask |= 1u;"),
-    "zeros_told_apart": ("return (double)f;", "return (f == 0.0f && signbit(f)) ? -1e-300 : (double)f;"),
-    "subnormals_flushed": ("return (double)f;", "return fpclassify(f) == FP_SUBNORMAL ? 0.0 : (double)f;"),
-    "fill_value": ("job->out_val[o] = 0x7FC0;", "job->out_val[o] = 0x0000;"),
+    "zeros_told_apart": ("memcpy(&f, &u, sizeof f);\n  return (double)f;",
+                         "memcpy(&f, &u, sizeof f);\n  return (f == 0.0f && signbit(f)) ? -1e-300 : (double)f;"),
+    "subnormals_flushed": ("memcpy(&f, &u, sizeof f);\n  return (double)f;",
+                           "memcpy(&f, &u, sizeof f);\n  return fpclassify(f) == FP_SUBNORMAL ? 0.0 : (double)f;"),
+    "fill_value": ("put_word(job->out_val, o, job->fill, job->word);", "put_word(job->out_val, o, 0, job->word);"),
     "fill_index": ("job->out_idx[o] = -1;", "job->out_idx[o] = 0;"),
     "mask_bits_swapped": ("(v > 0) ? 2u : 4u", "(v > 0) ? 4u : 2u"),
     "neginf_not_flagged": ("if (isinf(v)) mask |= (v > 0) ? 2u : 4u;", "if (isinf(v) && v > 0) mask |= 2u;"),
     "count_off_by_one": ("int64_t count = n < job->k ? n : job->k;", "int64_t count = n < job->k ? n : job->k - 1;"),
-    "stride_ignored": ("job->in + r * job->row_stride", "job->in + r * job->cols"),
+    "stride_ignored": ("const int64_t row = r * job->row_stride;", "const int64_t row = r * job->cols;"),
     "padding_read": [("for (int64_t c = 0; c < job->cols; ++c)",
                       "for (int64_t c = 0; c < job->row_stride; ++c)"),
                      ("(size_t)(job->cols > 0 ? job->cols : 1)", "(size_t)(job->row_stride > 0 ? job->row_stride : 1)")],
-    "value_from_entry_slot": ("job->out_val[o] = row[list[j].col];", "job->out_val[o] = row[j];"),
+    "value_from_entry_slot": ("word_at(job->in, row + list[j].col, job->word)", "word_at(job->in, row + j, job->word)"),
 }
 
 
