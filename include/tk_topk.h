@@ -121,6 +121,23 @@ tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
                          void *stream, const tk_options *opt);
 
 /*
+ * IEEE binary32 (fp32) rows: the same operation, outputs and rules with
+ * 32-bit inputs and entry values.  in: uint32 fp32 bit patterns, 4-byte
+ * aligned, row_stride in elements; out_val: uint32 [rows][k], the entries'
+ * own bits, empty slots 0x7FC00000.  Keys are 32 bits wide and composites 64,
+ * so one span may be any width; tk_options.spans accepts 0..64
+ * (TK_ERR_OPTION above).  tk_validate_f32 gives the guards alone.
+ */
+tk_status tk_topk_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                      int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream);
+tk_status tk_topk_f32_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                         int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                         void *stream, const tk_options *opt);
+tk_status tk_validate_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                          const int32_t *out_idx, const uint32_t *out_val, const int32_t *out_count,
+                          const uint32_t *out_nonfinite);
+
+/*
  * The host-side guards alone (no HIP call is made): returns the status
  * tk_topk_bf16 would return before launching anything.
  */

@@ -168,3 +168,21 @@ def test_sample_guards():
     assert vs(val=None) == NULL and vs(kept=None) == NULL
     assert vs(val=M_VAL + 1) == ALIGN and vs(tok=IDX + 2) == ALIGN
     assert vs(tok=M_IDX + 16) == ALIAS and vs(kept=IDX) == ALIAS
+
+
+def test_f32_guards():
+    def v32(rows=3, cols=100, stride=100, k=8, i=IN, idx=IDX, val=VAL, cnt=CNT, msk=MSK):
+        return tk.validate_f32(rows, cols, stride, k, i, idx, val, cnt, msk)
+
+    assert v32() == OK
+    assert v32(i=IN + 2) == ALIGN and v32(val=VAL + 2) == ALIGN  # 4-byte elements
+    assert v32(i=IN + 4) == OK
+    assert v32(k=0) == K and v32(stride=99) == SHAPE
+    # the input spans 4 bytes per element: an output 1000 bytes in overlaps it
+    assert v32(idx=IN + 1000) == ALIAS
+    assert tk.validate(3, 100, 100, 8, IN, IN + 1000, VAL, CNT, MSK) == OK  # bf16: 600 bytes of input only
+    lib = tk.load()
+    opt = tk.TkOptions(spans=65, exact=0)
+    import ctypes
+
+    assert lib.tk_topk_f32_ex(0, 100, 100, 8, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(opt)) == OPTION

@@ -1,0 +1,86 @@
+"""Parity of the HIP top-k on IEEE fp32 rows (tk_topk_f32) with the
+oracle's fp32 path, byte for byte: every family in fp32 form (random low
+fraction bits on the continuous families, exact ties on the others) over
+widths, strides, k, forced spans and misaligned rows; split counts equal
+the single-group control; the exact mode; the workload shapes at full size
+in fp32 form; rows wider than the bf16 span limit in one span."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_same, check_case, gpu_topk, log, need_gpu, upload
+from synth import CONFIGS, FAMILIES, bf16_to_f32_bits, family_rows, make_config_input
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = [1, 3, 4, 5, 65, 1000, 4099, 32768, 98592, 151936]
+KS = [1, 8, 20, 33, 64]
+SPANS = [0, 1, 3, 16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("family", sorted(FAMILIES))
+def test_family_widths_f32(family):
+    fi = sorted(FAMILIES).index(family)
+    for i, w in enumerate(WIDTHS):
+        stride = [w, w + 1, w + 3, -(-w // 64) * 64][(i + fi) % 4]
+        k = KS[(i + fi) % len(KS)]
+        spans = SPANS[(i + 2 * fi) % len(SPANS)]
+        if spans > w:
+            spans = 0
+        offset = (i + fi) % 4
+        m = family_rows(family, 3, w, stride, seed=700 + 10 * fi + i, fmt="f32")
+        what = f"f32 family={family} cols={w} stride={stride} k={k} spans={spans} offset={offset}"
+        log(what)
+        check_case(m, w, k, spans=spans, offset=offset, what=what, fmt="f32")
+
+
+@pytest.mark.parametrize("family", ["normal", "levels64", "mixed_nonfinite", "uniform_bits", "zeros_straddle",
+                                    "all_equal"])
+def test_split_and_exact_f32(family):
+    cols = 248320
+    m = family_rows(family, 3, cols, cols, seed=23, fmt="f32")
+    x = upload(m)
+    for k in (1, 20, 64):
+        want = oracle.topk_f32(m, cols, k)
+        for spans in (1, 2, 7, 12, 64):
+            log(f"f32 split family={family} k={k} spans={spans}")
+            assert_same(gpu_topk(m, cols, k, spans=spans, x=x, fmt="f32"), want, f"{family} k={k} spans={spans}")
+        assert_same(gpu_topk(m, cols, k, spans=1, x=x, fmt="f32", exact=True), want, f"{family} k={k} exact")
+
+
+def test_one_span_wider_than_the_bf16_limit():
+    cols = 600000
+    m = family_rows("normal", 2, cols, cols + 1, seed=4, fmt="f32")
+    for spans in (1, 0):
+        log(f"f32 wide spans={spans}")
+        check_case(m, cols, 40, spans=spans, what=f"f32 600000 spans={spans}", fmt="f32")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_configs_full_size_f32(name):
+    cfg = CONFIGS[name]
+    m = bf16_to_f32_bits(make_config_input(name), np.random.default_rng(31))
+    log(f"f32 config {name}")
+    want = oracle.topk_f32(m, cfg.cols, cfg.k)
+    x = upload(m)
+    for spans in (0, 1):
+        assert_same(gpu_topk(m, cfg.cols, cfg.k, spans=spans, x=x, fmt="f32"), want, f"f32 {name} spans={spans}")
+
+
+def test_equal_negative_rows_with_partial_waves():
+    """Rows of one negative value whose waves hold fewer vectors than lanes:
+    the zeros that out-of-range lanes read must never enter a batch (0.0
+    would outrank every entry)."""
+    for cols in (300, 1000, 4099):
+        for v in (-1.0, -3.5e-30):
+            m = np.full((2, cols), np.float32(v)).view(np.uint32)
+            for k in (1, 5, 64):
+                log(f"f32 equal negative cols={cols} v={v} k={k}")
+                check_case(m, cols, k, spans=1, what=f"f32 equal {v} cols={cols} k={k}", fmt="f32")
+                check_case(m, cols, k, what=f"f32 equal {v} cols={cols} k={k} auto", fmt="f32")

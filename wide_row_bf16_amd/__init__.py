@@ -33,7 +33,8 @@ FILL_IDX, FILL_VAL = -1, 0x7FC0
 
 # Every symbol the public header declares.
 EXPORTS = (
-    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_topk_f16", "tk_topk_f16_ex", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
+    "tk_topk_bf16", "tk_topk_bf16_ex", "tk_topk_f16", "tk_topk_f16_ex", "tk_topk_f32", "tk_topk_f32_ex",
+    "tk_validate_f32", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
     "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
 )
 
@@ -79,6 +80,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_topk_f16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.tk_topk_f16_ex.restype = i32
     lib.tk_topk_f16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
+    lib.tk_topk_f32.restype = i32
+    lib.tk_topk_f32.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.tk_topk_f32_ex.restype = i32
+    lib.tk_topk_f32_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
+    lib.tk_validate_f32.restype = i32
+    lib.tk_validate_f32.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.tk_validate_bf16.restype = i32
     lib.tk_validate_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.tk_topk_bf16_shard.restype = i32
@@ -136,7 +143,7 @@ def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr
     """Calls the C ABI on raw device pointers (fmt "bf16" or "f16"); returns
     the status code."""
     lib = load()
-    name = {"bf16": "tk_topk_bf16", "f16": "tk_topk_f16"}[fmt]
+    name = {"bf16": "tk_topk_bf16", "f16": "tk_topk_f16", "f32": "tk_topk_f32"}[fmt]
     if spans or exact:
         opt = TkOptions(spans=spans, exact=exact)
         return int(getattr(lib, name + "_ex")(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
@@ -165,8 +172,9 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
 
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
-    wanted = torch.bfloat16 if _fmt == "bf16" else torch.float16
-    if x.dtype not in (wanted, torch.int16, torch.uint16):
+    wanted = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[_fmt]
+    raw = (torch.int32, torch.uint32) if _fmt == "f32" else (torch.int16, torch.uint16)
+    if x.dtype not in (wanted,) + raw:
         raise TypeError(f"expected {_fmt} bit patterns, got {x.dtype}")
     if x.device.type != "cuda":
         raise ValueError("expected a tensor on a HIP device")
@@ -196,6 +204,16 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
     if status != TK_OK:
         raise TkError(status, "tk_topk_" + _fmt)
     return out
+
+
+def topk_f32(x, k: int, **kw) -> TopK:
+    """topk_bf16 for IEEE fp32 rows (tk_topk_f32); ``val`` holds fp32 values."""
+    return topk_bf16(x, k, _fmt="f32", **kw)
+
+
+def validate_f32(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr) -> int:
+    """The host-side guards of tk_topk_f32 on raw pointers (no HIP call)."""
+    return int(load().tk_validate_f32(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr))
 
 
 def topk_f16(x, k: int, **kw) -> TopK:

@@ -44,7 +44,7 @@ bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.h
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
 tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const void *in, const void *out_idx,
-                const void *out_val, const void *out_count, const void *out_nonfinite) {
+                const void *out_val, const void *out_count, const void *out_nonfinite, int eb = 2) {
   if (rows < 0 || cols < 0 || cols > INT32_MAX || stride < cols) return TK_ERR_SHAPE;
   if (k < 1 || k > kMaxK) return TK_ERR_K;
   if (rows == 0) return TK_OK;
@@ -52,13 +52,13 @@ tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const voi
   const int64_t big = std::numeric_limits<int64_t>::max() / 8;
   if (!mul_ok(rows - 1, stride, big) || (rows - 1) * stride > big - cols) return TK_ERR_SHAPE;
   if (!mul_ok(rows, k, big)) return TK_ERR_SHAPE;
-  if (((uintptr_t)in & 1) || ((uintptr_t)out_val & 1)) return TK_ERR_ALIGN;
+  if (((uintptr_t)in & (uintptr_t)(eb - 1)) || ((uintptr_t)out_val & (uintptr_t)(eb - 1))) return TK_ERR_ALIGN;
   if (((uintptr_t)out_idx & 3) || ((uintptr_t)out_count & 3) || ((uintptr_t)out_nonfinite & 3)) return TK_ERR_ALIGN;
   const int64_t in_elems = cols > 0 ? (rows - 1) * stride + cols : 0;
   const Range rs[5] = {
-      {(uintptr_t)in, (uintptr_t)in + (uintptr_t)(2 * in_elems)},
+      {(uintptr_t)in, (uintptr_t)in + (uintptr_t)(eb * in_elems)},
       {(uintptr_t)out_idx, (uintptr_t)out_idx + (uintptr_t)(4 * rows * k)},
-      {(uintptr_t)out_val, (uintptr_t)out_val + (uintptr_t)(2 * rows * k)},
+      {(uintptr_t)out_val, (uintptr_t)out_val + (uintptr_t)(eb * rows * k)},
       {(uintptr_t)out_count, (uintptr_t)out_count + (uintptr_t)(4 * rows)},
       {(uintptr_t)out_nonfinite, (uintptr_t)out_nonfinite + (uintptr_t)(4 * rows)},
   };
@@ -159,9 +159,9 @@ int32_t plan(int64_t rows, int64_t cols, int32_t compute_units) {
 // largest.  That count is about Poisson with mean k * sample / span, so j is
 // the smallest rank whose tail probability is at most kSpecFailure.  Returns
 // 0 when no rank below k qualifies (the exact floor, rank k, is then as good).
-int32_t spec_rank(int32_t k, int64_t span_cols) {
+int32_t spec_rank(int32_t k, int64_t span_cols, int64_t sample = kSampleElems) {
   if (span_cols <= 0) return 0;
-  const double lambda = (double)k * (double)kSampleElems / (double)span_cols;
+  const double lambda = (double)k * (double)sample / (double)span_cols;
   double p = std::exp(-lambda), cdf = p;  // P(X = 0), P(X <= 0)
   for (int32_t j = 1; j < k; ++j) {
     if (1.0 - cdf <= kSpecFailure) return j;  // P(X >= j)
@@ -393,6 +393,98 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   return result;
 }
 
+// fp32 rows: the same plan, guards and scratch layout as the bf16 split path;
+// every split row is folded by its last scan workgroup (at most kMergeGroup
+// spans: the fp32 scan has no span width limit, so a plan never needs more).
+tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint32_t *in, int32_t *out_idx,
+                uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
+                const tk_options *opt) {
+  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4);
+  if (st != TK_OK) return st;
+  int32_t forced = 0, exact = 0;
+  if (opt) {
+    for (int i = 0; i < 6; ++i)
+      if (opt->reserved[i] != 0) return TK_ERR_OPTION;
+    if (opt->exact != 0 && opt->exact != 1) return TK_ERR_OPTION;
+    exact = opt->exact;
+    forced = opt->spans;
+    if (forced < 0 || forced > kMergeGroup) return TK_ERR_OPTION;
+    if (forced > 1 && cols > 0 && forced > cols) return TK_ERR_OPTION;
+  }
+  if (rows == 0) return TK_OK;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
+  if (spans > kMergeGroup) spans = kMergeGroup;
+
+  tk::ScanArgs32 sa{};
+  sa.in = in;
+  sa.cols = cols;
+  sa.stride = stride;
+  sa.k = k;
+  sa.spans = spans;
+  sa.exact = exact;
+  // the pooled sample holds half as many fp32 elements as bf16 ones
+  sa.spec_rank = exact ? 0 : spec_rank(k, cols / spans, kSampleElems / 2);
+  sa.out_idx = out_idx;
+  sa.out_val = out_val;
+  sa.out_count = out_count;
+  sa.out_nonfinite = out_nonfinite;
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
+  if (spans == 1) {
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+      const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+      sa.row0 = r0;
+      if (tk::launch_span_scan32(sa, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
+    }
+    return TK_OK;
+  }
+  const int64_t batch_cap = rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
+  const int64_t batch = rows < batch_cap ? rows : batch_cap;
+  const size_t counters_bytes = align256((size_t)kFusedMaxRows * sizeof(int32_t));
+  const size_t nlists = (size_t)batch * (size_t)spans;
+  const size_t off_list = counters_bytes;
+  const size_t off_count = align256(off_list + nlists * (size_t)k * sizeof(uint64_t));
+  const size_t off_flags = align256(off_count + nlists * sizeof(int32_t));
+  const size_t total = align256(off_flags + nlists * sizeof(uint32_t));
+  keep_pool(dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  tk_status sst = TK_OK;
+  bool fresh = false;
+  void *scratch = cached_scratch(dev, stream, total, &sst, &fresh);
+  if (sst != TK_OK) return sst;
+  const bool owned = scratch == nullptr;
+  if (owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
+  char *base = (char *)scratch;
+  int32_t *counters = (int32_t *)base;
+  if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
+    if (owned) hipFreeAsync(scratch, stream);
+    return TK_ERR_DEVICE;
+  }
+  tk_status result = TK_OK;
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    tk::ScanArgs32 b = sa;
+    b.in = in + r0 * stride;
+    b.row0 = 0;
+    b.span_list = (uint64_t *)(base + off_list);
+    b.span_count = (int32_t *)(base + off_count);
+    b.span_flags = (uint32_t *)(base + off_flags);
+    b.row_done = counters;
+    b.out_idx = out_idx + r0 * k;
+    b.out_val = out_val + r0 * k;
+    b.out_count = out_count + r0;
+    b.out_nonfinite = out_nonfinite + r0;
+    if (tk::launch_span_scan32(b, nr, stream) != hipSuccess) {
+      result = TK_ERR_DEVICE;
+      break;
+    }
+  }
+  if (owned && hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  return result;
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +510,23 @@ tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
                          int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                          void *stream, const tk_options *opt) {
   return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, opt, 0, 0x7C00u);
+}
+
+tk_status tk_topk_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                      int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream) {
+  return run32(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr);
+}
+
+tk_status tk_topk_f32_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                         int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                         void *stream, const tk_options *opt) {
+  return run32(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, opt);
+}
+
+tk_status tk_validate_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
+                          const int32_t *out_idx, const uint32_t *out_val, const int32_t *out_count,
+                          const uint32_t *out_nonfinite) {
+  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4);
 }
 
 tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,

@@ -24,7 +24,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kFusedMaxRows = 4096;             // rows per launch of the fused (single-dispatch) split path
 constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
-constexpr int kSampleElems = 4 * 4 * 64 * 8;    // pooled sample: the first chunk of each wave
+constexpr int kSampleElems = kWgWaves * kChunkVecs * kWave * kVecElems;  // pooled sample: each wave's first chunk
 constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
 
 static_assert(kMaxK == (int)TK_MAX_K, "public and internal max k differ");

@@ -1,0 +1,533 @@
+// Exact row-wise top-k of IEEE fp32 rows (gfx950): the same operation as the
+// bf16 scan (TensorFold PR #713, change 3, and its Exactness table: score
+// descending, lower column first on ties, NaN excluded and flagged,
+// infinities ranked, zeros equal), for 32-bit logits.
+//
+// Order key.  An fp32 pattern b with magnitude m = b & 0x7FFFFFFF maps to
+// 0x80000000 + m (sign clear) or 0x80000000 - m (sign set): monotone in value,
+// +0 and -0 share 0x80000000, -inf -> 0x00800000, +inf -> 0xFF800000, NaN
+// (m > 0x7F800000) -> 0, never kept.  Composites are 64-bit, key << 32 |
+// (0xFFFFFFFF - column) with the absolute column, in the wave lists as in the
+// span lists: a strict total order equal to (score desc, column asc), with
+// no limit on the width one wave may scan.
+//
+// The scan follows the bf16 kernel's design (one workgroup = four wave64s per
+// (row, span), a per-wave list of the 64 best composites in registers, one
+// lane per entry, a raw-bit filter that skips vectors without a candidate,
+// floors from a pooled first-chunk sample, thresholds shared in LDS, issue
+// priority falling with progress, a rank merge in LDS, and the last
+// workgroup of a split row folding the span lists), with four fp32 elements
+// per 16-byte vector and 64-bit list entries.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tk_config.h"
+#include "tk_launch.h"
+#include "tk_topk.h"
+
+namespace tk {
+namespace {
+
+#include "tk_wave.h"
+
+constexpr int kElems32 = 4;  // fp32 per 16-byte vector
+
+__device__ __forceinline__ uint32_t key32(uint32_t b) {
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  const uint32_t key = (b & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
+  return mag > 0x7F800000u ? 0u : key;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  return ((uint64_t)readlane((uint32_t)(v >> 32), l) << 32) | readlane((uint32_t)v, l);
+}
+
+__device__ __forceinline__ uint64_t lanes_ugt64(uint64_t a, uint64_t b) { return ballot(a > b); }
+
+// One 64-bit composite into the descending list (see insert_one).
+__device__ __forceinline__ uint64_t insert_one64(uint64_t list, uint64_t c) {
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)(uint32_t)list, 0x138, 0xF, 0xF, false);
+  const uint32_t phi =
+      (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)(uint32_t)(list >> 32), 0x138, 0xF, 0xF, false);
+  const uint64_t prev = ((uint64_t)phi << 32) | plo;
+  const uint64_t lo = prev < c ? prev : c;
+  return list > lo ? list : lo;
+}
+
+// Descending bitonic sort of one 64-bit value per lane (the stages of sort64_desc).
+__device__ __forceinline__ uint64_t sort64_desc64(uint64_t v, const Xchg &x) {
+  v = cx_stage64<1, 1>(v, x);
+  v = cx_stage64<3, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  v = cx_stage64<7, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  v = cx_stage64<15, 8>(v, x);
+  v = cx_stage64<4, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  v = cx_stage64<31, 16>(v, x);
+  v = cx_stage64<8, 8>(v, x);
+  v = cx_stage64<4, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  v = cx_stage64<63, 32>(v, x);
+  v = cx_stage64<16, 16>(v, x);
+  v = cx_stage64<8, 8>(v, x);
+  v = cx_stage64<4, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  return v;
+}
+
+struct Wave32 {
+  uint64_t list;   // lane i: i-th best composite so far, 0 = empty
+  uint64_t kth;    // wave-uniform copy of list[k - 1]
+  uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of the workgroup
+  uint32_t floor;  // wave-uniform floor: only keys > floor are kept (0 = none)
+  uint32_t flags;  // wave-uniform NaN / -inf flags seen so far
+  int km1, qm1, wave;
+  uint32_t *tau;   // LDS: published k-th and ceil(k/4)-th keys of the waves
+  Xchg x;
+};
+
+// Adds the candidates c of lanes m (and of no other lane): one bitonic batch
+// when many, else one insertion each (against a k-th refreshed only
+// afterwards: see offer).
+__device__ __forceinline__ void offer64(Wave32 &w, uint64_t c, uint64_t m) {
+  if (__popcll(m) >= kBatchInsert) {
+    const bool take = (m >> lane_id()) & 1ull;
+    w.list = merge_sorted64(w.list, sort64_desc64(take ? c : 0, w.x), w.x);
+  } else {
+    do {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      w.list = insert_one64(w.list, readlane64(c, l));
+    } while (m);
+  }
+  w.kth = readlane64(w.list, w.km1);
+}
+
+// Threshold sharing, as in the bf16 scan (shared_bound / publish there).
+__device__ __forceinline__ uint32_t shared_bound32(const uint32_t *s_tau, int wave) {
+  uint32_t ext = 0, qmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    const uint32_t t = __hip_atomic_load(&s_tau[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t q = __hip_atomic_load(&s_tau[kWgWaves + o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t b = o < wave ? t : (t > 0 ? t - 1 : 0u);
+    if (o != wave) ext = max(ext, b);
+    qmin = min(qmin, q);
+  }
+  if (qmin > 0) ext = max(ext, qmin - 1);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ext);
+}
+
+__device__ __forceinline__ void publish32(const Wave32 &w) {
+  const uint32_t q = (uint32_t)(readlane64(w.list, w.qm1) >> 32);
+  if (lane_id() == 0) {
+    __hip_atomic_store(&w.tau[w.wave], (uint32_t)(w.kth >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&w.tau[kWgWaves + w.wave], q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Raw-bit filter from T = max(k-th kept key, ext): an element may matter only
+// if its key exceeds T.  T >= 2^31: bits, as int32, above T - 2^31 (only
+// non-negative patterns, +NaN included, pass).  T < 2^31: bits, as uint32,
+// at most 0xFFFFFFFF - T (every non-negative pattern passes, and negatives
+// whose magnitude is below 2^31 - T).
+struct Filter32 {
+  bool nonneg;
+  int32_t t32;
+  uint32_t tum1;
+  bool check_flags;  // some of -inf / negative NaN not flagged yet
+  uint32_t ftrip;    // patterns >= ftrip: -inf (0xFF800000) or negative NaN
+};
+
+__device__ __forceinline__ Filter32 make_filter32(const Wave32 &w) {
+  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(w.kth >> 32));
+  const uint32_t t = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
+  const uint32_t flags = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags);
+  Filter32 f;
+  f.nonneg = t >= 0x80000000u;
+  f.t32 = (int32_t)(t - 0x80000000u);
+  f.tum1 = 0xFFFFFFFFu - t;
+  f.check_flags = (flags & (kNan | kNinf)) != (kNan | kNinf);
+  f.ftrip = (flags & kNinf) ? 0xFF800001u : 0xFF800000u;
+  return f;
+}
+
+__device__ __forceinline__ uint64_t value_trip(uint4 d, const Filter32 &f) {
+  if (f.nonneg) {
+    const int32_t a = max(max((int32_t)d.x, (int32_t)d.y), max((int32_t)d.z, (int32_t)d.w));
+    return __builtin_amdgcn_sicmp(a, f.t32, 38);  // >
+  }
+  const uint32_t a = min(min(d.x, d.y), min(d.z, d.w));
+  return __builtin_amdgcn_uicmp(a, f.tum1, 37);  // <=
+}
+
+__device__ __forceinline__ uint64_t flag_trip(uint4 d, const Filter32 &f) {
+  if (!f.check_flags) return 0;
+  const uint32_t a = max(max(d.x, d.y), max(d.z, d.w));
+  return lanes_uge(a, f.ftrip);
+}
+
+// Exact path for one vector of four elements per lane (lanes `lanes`):
+// per element, the composites of all lanes, then the lanes that beat the
+// k-th -- one insertion each, or one batch when many.
+__device__ __forceinline__ void take_vector32(Wave32 &w, uint4 d, uint32_t col0, uint64_t lanes) {
+  // one element position per iteration: a runtime loop (rotating the
+  // vector's words) keeps a single copy of the insertion code
+#pragma unroll 1
+  for (int e = 0; e < kElems32; ++e) {
+    const uint32_t b = d.x;
+    d = make_uint4(d.y, d.z, d.w, d.x);
+    const uint32_t key = key32(b);
+    if (lanes & ballot(key == 0)) w.flags |= kNan;
+    if (lanes & ballot(b == 0xFF800000u)) w.flags |= kNinf;
+    const uint64_t c = key > w.ext ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e)) : 0;
+    const uint64_t m = lanes & lanes_ugt64(c, w.kth);
+    if (m) offer64(w, c, m);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer format on gfx9-family parts
+constexpr int kLoadPolicy = 2;            // nontemporal: the input is read once
+
+// Vectors [first, first + kChunkVecs * 64) of the wave's nvec at vp (lane l's
+// vector u is first + u * 64 + l); vectors at or past nvec read zeros.
+__device__ __forceinline__ void load_chunk32(uint4 (&dst)[kChunkVecs], const uint4 *vp, uint32_t nvec, uint32_t first,
+                                             uint32_t lane_off) {
+  first = (uint32_t)__builtin_amdgcn_readfirstlane((int)first);
+  nvec = (uint32_t)__builtin_amdgcn_readfirstlane((int)nvec);
+  uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(nvec - min(first, nvec)));
+  left = min(left, (uint32_t)(kChunkVecs * kWave));
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vp + first), (short)0, (int)(left * 16u), kBufferWord3);
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const u32x4 x =
+        __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(lane_off + (uint32_t)(u * kWave * 16)), 0, kLoadPolicy);
+    dst[u] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_max_key32(const uint4 (&v)[kChunkVecs], uint32_t nvec) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint32_t mu = max(max(key32(v[u].x), key32(v[u].y)), max(key32(v[u].z), key32(v[u].w)));
+    if ((uint32_t)(u * kWave + lane_id()) < nvec) m = max(m, mu);
+  }
+  return m;
+}
+
+// One chunk: trips against the thresholds at its start (they only rise),
+// then the exact path for the tripped vectors in order.
+__device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
+                                             uint32_t col_first) {
+  w.ext = max(shared_bound32(w.tau, w.wave), w.floor);
+  const Filter32 f = make_filter32(w);
+  const uint32_t l = (uint32_t)lane_id();
+  uint64_t any = 0, trip[kChunkVecs];
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    trip[u] = (value_trip(v[u], f) | flag_trip(v[u], f)) & lanes_ult(first + (uint32_t)(u * kWave) + l, nvec);
+    any |= trip[u];
+  }
+  if (!any) return;
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // rotated once per vector: one copy of the exact path
+  uint64_t t0 = trip[0], t1 = trip[1], t2 = trip[2], t3 = trip[3];
+  uint32_t col = col_first + kElems32 * (first + l);
+#pragma unroll 1
+  for (int u = 0; u < kChunkVecs; ++u) {
+    if (t0) take_vector32(w, x0, col, t0);
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+    t0 = t1;
+    t1 = t2;
+    t2 = t3;
+    t3 = 0;
+    if (!(t0 | t1 | t2)) break;
+    col += kElems32 * kWave;
+  }
+  publish32(w);
+}
+
+// Streams nvec vectors from vp (element 0 is column col_first), two chunks in
+// flight; A holds the first chunk, already loaded.  Issue priority falls
+// with progress, as in the bf16 scan.
+__device__ __forceinline__ void take_body32(Wave32 &w, const uint4 *vp, uint32_t nvec, uint32_t col_first,
+                                            uint4 (&A)[kChunkVecs]) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+  const uint32_t lane_off = (uint32_t)lane_id() * 16u;
+  uint4 B[kChunkVecs];
+  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;
+  __builtin_amdgcn_s_setprio(3);
+  for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+    if (first >= q3) __builtin_amdgcn_s_setprio(0);
+    else if (first >= q2) __builtin_amdgcn_s_setprio(1);
+    else if (first >= q1) __builtin_amdgcn_s_setprio(2);
+    load_chunk32(B, vp, nvec, first + kStep, lane_off);
+    take_chunk32(w, A, first, nvec, col_first);
+    if (first + kStep >= nvec) break;
+    load_chunk32(A, vp, nvec, first + 2 * kStep, lane_off);
+    take_chunk32(w, B, first + kStep, nvec, col_first);
+  }
+}
+
+// Columns [lo, hi) one per lane (row edges outside the 16-byte grid).
+__device__ void take_columns32(Wave32 &w, const uint32_t *row, int64_t lo, int64_t hi) {
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? row[col] : 0u;
+    const uint32_t key = key32(b);
+    if (ballot(valid && key == 0)) w.flags |= kNan;
+    if (ballot(valid && b == 0xFF800000u)) w.flags |= kNinf;
+    const uint64_t c = (valid && key > w.ext) ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (uint32_t)col) : 0;
+    const uint64_t m = lanes_ugt64(c, w.kth);
+    if (m) offer64(w, c, m);
+  }
+}
+
+__device__ __forceinline__ int32_t col_of32(uint64_t x) { return (int32_t)(0xFFFFFFFFu - (uint32_t)x); }
+
+// fp32 bits of an entry: the key is invertible except for the zeros' shared
+// key, whose sign is read back from the input.
+__device__ __forceinline__ uint32_t value_bits32(uint64_t x, const uint32_t *row) {
+  const uint32_t key = (uint32_t)(x >> 32);
+  if (key > 0x80000000u) return key - 0x80000000u;
+  if (key < 0x80000000u) return 0x80000000u | (0x80000000u - key);
+  return row[col_of32(x)];
+}
+
+__device__ __forceinline__ int count_beating32(const uint64_t *list, int n, uint64_t x) {
+  int lo = 0, hi = n;  // entries [0, lo) beat x, [hi, n) do not
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The last workgroup of a split row folds the row's span lists (see
+// fold_row_if_last in the bf16 scan: agent-scope atomic stores and loads, an
+// arrival counter that returns to zero).
+__device__ __forceinline__ void fold_row32_if_last(const ScanArgs32 &a, int64_t r, int S, const uint32_t *row,
+                                                   int wave, int l) {
+  __shared__ int s_last;
+  __shared__ uint64_t s_acc[kWgWaves][kWave];
+  __shared__ int32_t s_cnt[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+  const int64_t rb = r - a.row0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const Xchg x = make_xchg();
+  uint64_t acc = 0;
+  int cnt = 0;
+  uint32_t fl = 0;
+  for (int i = wave; i < S; i += kWgWaves) {
+    const int64_t sb = r * S + i;
+    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t v =
+        l < c ? __hip_atomic_load(&a.span_list[sb * a.k + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    acc = i == wave ? v : merge_sorted64(acc, v, x);
+    cnt += c;
+  }
+  s_acc[wave][l] = acc;
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_fl[wave] = fl;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int o = 1; o < kWgWaves; ++o) {
+    acc = merge_sorted64(acc, s_acc[o][l], x);
+    cnt += s_cnt[o];
+    fl |= s_fl[o];
+  }
+  const int k = a.k;
+  if (cnt > k) cnt = k;
+  const int64_t ob = r * k;
+  if (l < k) {
+    if (l < cnt) {
+      a.out_idx[ob + l] = col_of32(acc);
+      a.out_val[ob + l] = value_bits32(acc, row);
+    } else {
+      a.out_idx[ob + l] = TK_FILL_IDX;
+      a.out_val[ob + l] = 0x7FC00000u;
+    }
+  }
+  if (l == 0) {
+    a.out_count[r] = cnt;
+    a.out_nonfinite[r] = fl;
+    __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
+  __shared__ uint64_t s_list[kWgWaves][kWave];
+  __shared__ int32_t s_count[kWgWaves];
+  __shared__ uint32_t s_flags[kWgWaves];
+  __shared__ uint32_t s_tau[2 * kWgWaves];
+  __shared__ uint32_t s_samp[kWgWaves][kWave];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const uint32_t *row = a.in + r * a.stride;
+
+  // The row's 16-byte grid: vector j covers columns [a0 + 4j, a0 + 4j + 4).
+  const int64_t a0 = (int64_t)((4u - (uint32_t)(((uintptr_t)row >> 2) & 3u)) & 3u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kElems32 : 0;
+  int64_t j0 = 0, j1 = 0, head_lo = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kElems32 * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+
+  // Floors from a pooled first-chunk sample, as in the bf16 scan.
+  const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t wn = (uint32_t)(wv1 - wv0);
+  uint4 A[kChunkVecs];
+  if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
+  const bool speculate = a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
+  uint32_t exact_floor, spec_floor;
+  {
+    const Xchg x = make_xchg();
+    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key32(A, wn) : 0u, x);
+    __syncthreads();
+    uint32_t v[kWgWaves];
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o) v[o] = s_samp[o][l];
+#pragma unroll
+    for (int step = 1; step < kWgWaves; step *= 2)
+#pragma unroll
+      for (int o = 0; o + step < kWgWaves; o += 2 * step)
+        v[o] = bitonic_merge64_desc(max(v[o], partner<63>(v[o + step], x)), x);
+    const uint32_t te = readlane(v[0], a.k - 1);
+    const uint32_t ts = speculate ? readlane(v[0], a.spec_rank - 1) : 0u;
+    exact_floor = te > 0 ? te - 1 : 0;
+    spec_floor = ts > 0 ? ts - 1 : 0;
+  }
+  uint32_t floor = exact_floor;
+  bool verify = false;
+  if (spec_floor > exact_floor) {
+    floor = spec_floor;
+    verify = true;
+  }
+
+  int total = 0;
+  uint32_t flags = 0;
+  for (;;) {
+    if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
+    __syncthreads();
+    Wave32 w;
+    w.list = 0;
+    w.kth = 0;
+    w.ext = floor;
+    w.floor = floor;
+    w.flags = 0;
+    w.km1 = a.k - 1;
+    w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
+    w.wave = wave;
+    w.tau = s_tau;
+    w.x = make_xchg();
+
+    if (wave == 0 && head_hi > head_lo) take_columns32(w, row, head_lo, head_hi);
+    if (wn > 0) take_body32(w, wvp, wn, (uint32_t)(a0 + kElems32 * wv0), A);
+    if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns32(w, row, tail_lo, tail_hi);
+
+    const uint64_t valid_mask = ballot(w.list != 0);
+    s_list[wave][l] = w.list;
+    if (l == 0) {
+      const int cnt = __popcll(valid_mask);
+      s_count[wave] = cnt < a.k ? cnt : a.k;
+      s_flags[wave] = w.flags | ((uint32_t)(readlane64(w.list, 0) >> 32) == 0xFF800000u ? kPinf : 0u);
+    }
+    __syncthreads();
+
+    total = 0;
+    flags = 0;
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o) {
+      total += s_count[o];
+      flags |= s_flags[o];
+    }
+    if (!verify || total >= a.k) break;  // exact, or the speculation verified
+    floor = exact_floor;                 // too few entries reach the speculative floor
+    verify = false;
+    if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
+    __syncthreads();
+  }
+  if (total > a.k) total = a.k;
+
+  const uint64_t x = s_list[wave][l];
+  const bool mine = l < s_count[wave];
+  int rank = l;
+  if (mine) {
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o)
+      if (o != wave) rank += count_beating32(s_list[o], s_count[o], x);
+  }
+
+  if (S == 1) {
+    const int64_t ob = r * a.k;
+    if (mine && rank < a.k) {
+      a.out_idx[ob + rank] = col_of32(x);
+      a.out_val[ob + rank] = value_bits32(x, row);
+    }
+    const int t = threadIdx.x;
+    if (t >= total && t < a.k) {
+      a.out_idx[ob + t] = TK_FILL_IDX;
+      a.out_val[ob + t] = 0x7FC00000u;
+    }
+    if (t == 0) {
+      a.out_count[r] = total;
+      a.out_nonfinite[r] = flags;
+    }
+  } else {
+    const int64_t sb = r * S + s;
+    if (mine && rank < a.k)
+      __hip_atomic_store(&a.span_list[sb * a.k + rank], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    fold_row32_if_last(a, r, S, row, wave, l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
+  const int64_t blocks = rows_in_launch * a.spans;
+  hipLaunchKernelGGL(span_scan32_kernel, dim3((uint32_t)blocks), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tk

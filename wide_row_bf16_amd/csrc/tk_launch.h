@@ -95,6 +95,30 @@ struct SampleArgs {
 hipError_t launch_sample(const SampleArgs &a, hipStream_t stream);
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
+
+// The fp32 scan (tk_f32.hip): as ScanArgs with 32-bit inputs and entry
+// values; split rows (2 <= spans <= kMergeGroup) are always folded by their
+// last workgroup (row_done required then).
+struct ScanArgs32 {
+  const uint32_t *in;
+  int64_t row0;
+  int64_t cols;
+  int64_t stride;
+  int32_t k;
+  int32_t spans;
+  int32_t exact;
+  int32_t spec_rank;
+  int32_t *out_idx;
+  uint32_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+  uint64_t *span_list;
+  int32_t *span_count;
+  uint32_t *span_flags;
+  int32_t *row_done;
+};
+
+hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
 
