@@ -95,11 +95,18 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
  *   exact  0 = automatic; 1 = never take the speculative floor (wide spans
  *          otherwise skip elements below a floor estimated from a sample and
  *          verify it afterwards, scanning again when it does not hold).
+ *   general  0 = automatic; 1 = k == 1 runs the general top-k scan instead of
+ *          the argmax scan (the control of that fast path).  bf16 and fp16
+ *          only; fp32 rows accept it and always run their general scan.
+ *          With k == 1 the argmax scan takes spans (forced or planned) up to
+ *          64; above that the general scan runs.
+ *   Values other than 0 and 1 for exact and general give TK_ERR_OPTION.
  */
 typedef struct tk_options {
   int32_t spans;
   int32_t exact;
-  int32_t reserved[6]; /* must be zero */
+  int32_t general;
+  int32_t reserved[5]; /* must be zero */
 } tk_options;
 
 tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
@@ -147,7 +154,8 @@ tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32
 
 /*
  * The span count the automatic plan picks for a shape on a GPU with
- * `compute_units` CUs (host-only arithmetic; no HIP call).
+ * `compute_units` CUs (host-only arithmetic; no HIP call).  For k == 1 that
+ * is the plan of the argmax scan (bf16 and fp16 rows).
  */
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units);
 

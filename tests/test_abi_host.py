@@ -104,6 +104,47 @@ def test_plan():
             assert 1 <= s and (cols // 8 + s - 1) // s <= tk.max_span_cols() // 8
 
 
+def test_plan_k1():
+    # k = 1 (argmax scan): S = round(sqrt(cols / (150 rows))) on few rows of at
+    # least 32768 columns, spans at least 2048 columns wide, at most 64
+    assert tk.plan_spans(1024, 151936, 1) == 1
+    assert tk.plan_spans(256, 151936, 1) == 1
+    assert tk.plan_spans(15, 98592, 1) == 7          # sqrt(43.8) = 6.6
+    assert tk.plan_spans(16, 248320, 1) == 10
+    assert tk.plan_spans(64, 151936, 1) == 4
+    assert tk.plan_spans(1, 151936, 1) == 32
+    assert tk.plan_spans(1, 32767, 1) == 1 and tk.plan_spans(1, 4096, 1) == 1
+    assert tk.plan_spans(1, 10**6, 1) == 64
+    assert tk.plan_spans(4, 10**9, 1) >= 65          # beyond 64 spans: the general scan's plan
+    for rows in (1, 3, 15, 64, 255, 256, 511, 512, 1000):
+        for cols in (0, 1, 2048, 4095, 32768, 70000, 151936, 248320, 600000):
+            s = tk.plan_spans(rows, cols, 1)
+            assert 1 <= s <= 64 and (s == 1 or cols // s >= 2048)
+            assert rows < 256 or s == max(1, -(-(cols // 8) // 32640))  # only the span width limit
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16", "f32"])
+def test_option_fields(fmt):
+    """tk_options: exact and general take 0 or 1, the reserved words must be
+    zero; checked before any device work (rows == 0)."""
+    import ctypes
+
+    lib = tk.load()
+    fn = getattr(lib, f"tk_topk_{fmt}_ex")
+
+    def call(**kw):
+        opt = tk.TkOptions(**{k: v for k, v in kw.items() if k != "reserved"})
+        for i, v in kw.get("reserved", {}).items():
+            opt.reserved[i] = v
+        return fn(0, 100, 100, 1, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(opt))
+
+    assert ctypes.sizeof(tk.TkOptions) == 32
+    assert call() == OK and call(general=1) == OK and call(exact=1, general=1, spans=4) == OK
+    assert call(general=2) == OPTION and call(general=-1) == OPTION and call(exact=2) == OPTION
+    for i in range(5):
+        assert call(reserved={i: 1}) == OPTION
+
+
 def test_oracle_and_library_share_nothing():
     """The oracle and the HIP path are built from disjoint sources."""
     import oracle

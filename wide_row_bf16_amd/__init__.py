@@ -46,7 +46,8 @@ class TkError(RuntimeError):
 
 
 class TkOptions(ctypes.Structure):
-    _fields_ = [("spans", ctypes.c_int32), ("exact", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("spans", ctypes.c_int32), ("exact", ctypes.c_int32), ("general", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 class TopK(NamedTuple):
@@ -139,13 +140,13 @@ def validate(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mas
 
 
 def topk_bf16_raw(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream=0, spans=0,
-                  exact=0, fmt="bf16") -> int:
+                  exact=0, fmt="bf16", general=0) -> int:
     """Calls the C ABI on raw device pointers (fmt "bf16" or "f16"); returns
     the status code."""
     lib = load()
     name = {"bf16": "tk_topk_bf16", "f16": "tk_topk_f16", "f32": "tk_topk_f32"}[fmt]
-    if spans or exact:
-        opt = TkOptions(spans=spans, exact=exact)
+    if spans or exact or general:
+        opt = TkOptions(spans=spans, exact=exact, general=general)
         return int(getattr(lib, name + "_ex")(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr,
                                               stream, ctypes.byref(opt)))
     return int(getattr(lib, name)(rows, cols, row_stride, k, in_ptr, idx_ptr, val_ptr, count_ptr, mask_ptr, stream))
@@ -158,13 +159,15 @@ def _current_stream_handle(torch, dev: int) -> int:
     return int(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool = False, out: TopK | None = None,
-              stream=None, _fmt: str = "bf16") -> TopK:
+def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool = False, general: bool = False,
+              out: TopK | None = None, stream=None, _fmt: str = "bf16") -> TopK:
     """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
 
     ``cols`` limits the scan to the first ``cols`` columns (default: all);
     ``spans`` forces the row split (0 = automatic, 1 = one workgroup per row);
     ``exact`` turns off the speculative floor (the result is the same);
+    ``general`` makes k = 1 run the general scan instead of the argmax scan
+    (the same result; the control of that fast path);
     ``out`` reuses preallocated outputs; ``stream`` is a torch.cuda.Stream
     (default: the current stream).
     """
@@ -195,7 +198,7 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
     args = (rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
-            out.nonfinite.data_ptr(), handle, spans, int(exact), _fmt)
+            out.nonfinite.data_ptr(), handle, spans, int(exact), _fmt, int(general))
     if dev == torch.cuda.current_device():
         status = topk_bf16_raw(*args)
     else:

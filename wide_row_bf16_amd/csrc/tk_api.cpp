@@ -251,18 +251,130 @@ void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st, b
   return slot->ptr;
 }
 
+// With g_scratch_mu held: `total` bytes of device scratch for one call, whose
+// first kFusedMaxRows int32 are the fused merges' arrival counters (zero
+// between calls; zeroed here whenever the buffer is new).  The stream's cached
+// buffer, or one owned by the call (*owned: the caller frees it,
+// stream-ordered, after its last launch).
+tk_status acquire_scratch(int dev, hipStream_t stream, size_t total, char **base, bool *owned) {
+  tk_status sst = TK_OK;
+  bool fresh = false;
+  void *scratch = cached_scratch(dev, stream, total, &sst, &fresh);
+  if (sst != TK_OK) return sst;
+  *owned = scratch == nullptr;
+  if (*owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
+  if ((*owned || fresh) && tk::launch_zero_fill((int32_t *)scratch, kFusedMaxRows, stream) != hipSuccess) {
+    if (*owned) hipFreeAsync(scratch, stream);
+    return TK_ERR_DEVICE;
+  }
+  *base = (char *)scratch;
+  return TK_OK;
+}
+
+// k = 1: span plan of the argmax scan.  On few rows a call is latency bound:
+// each extra workgroup costs about 9 ns of dispatch, while a workgroup streams
+// its span with a fixed number of bytes in flight, so its time grows with the
+// span width; a split also adds the fold (~1.2 us: slot store, arrival count,
+// slot loads).  Minimising rows * S * beta + gamma * cols / S gives S = sqrt(cols /
+// (c * rows)); c = 150 matched the measured best span count on MI355X within
+// 0.2 us for 1-32 rows of 98592-248320 columns (15 x 98592: 7 spans, 7.2 us
+// device time; 64 x 151936: 4; 1 x 151936: 32).  Rows of fewer than
+// kArgmaxSplitCols columns, and calls with a workgroup for every CU, are not
+// split.  Spans stay at least kArgmaxMinSpanCols wide (each wave reads at
+// least one 16-byte vector per lane) and at most kMergeGroup per row (the
+// last workgroup takes the maximum of one slot per lane).  A result above
+// kMergeGroup (only from the span width limit, for rows over 16.7 M columns)
+// sends the call to the general scan.
+constexpr int64_t kArgmaxMinSpanCols = 2048;
+constexpr int64_t kArgmaxSplitCols = 32768;
+constexpr double kArgmaxSpanScale = 150.0;
+
+int32_t plan_argmax(int64_t rows, int64_t cols, int32_t compute_units) {
+  if (cols <= 0 || rows <= 0) return 1;
+  int64_t s = 1;
+  if (rows < compute_units && cols >= kArgmaxSplitCols) {
+    s = (int64_t)(std::sqrt((double)cols / (kArgmaxSpanScale * (double)rows)) + 0.5);
+    const int64_t by_width = cols / kArgmaxMinSpanCols;
+    if (s > by_width) s = by_width;
+    if (s > kMergeGroup) s = kMergeGroup;
+  }
+  const int64_t need = min_spans(cols);
+  if (s < need) s = need;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+// k = 1 through argmax_scan_kernel: spans == 1 writes the outputs directly;
+// 2 <= spans <= kMergeGroup writes one slot per (row, span) after the arrival
+// counters, in batches of at most kFusedMaxRows rows.
+tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t *in, int32_t *out_idx,
+                     uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, hipStream_t stream, int dev,
+                     int32_t spans, int64_t col_base, uint32_t inf) {
+  tk::ArgmaxArgs a{};
+  a.in = in;
+  a.cols = cols;
+  a.stride = stride;
+  a.spans = spans;
+  a.inf = inf;
+  a.col_base = col_base;
+  a.out_idx = out_idx;
+  a.out_val = out_val;
+  a.out_count = out_count;
+  a.out_nonfinite = out_nonfinite;
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
+  if (spans == 1) {
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+      const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+      a.row0 = r0;
+      if (tk::launch_argmax(a, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
+    }
+    return TK_OK;
+  }
+  const int64_t batch_cap = rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
+  const int64_t batch = rows < batch_cap ? rows : batch_cap;
+  const size_t off_slot = align256((size_t)kFusedMaxRows * sizeof(int32_t));
+  const size_t total = align256(off_slot + (size_t)batch * (size_t)spans * sizeof(uint64_t));
+  keep_pool(dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  char *base = nullptr;
+  bool owned = false;
+  const tk_status sst = acquire_scratch(dev, stream, total, &base, &owned);
+  if (sst != TK_OK) return sst;
+  tk_status result = TK_OK;
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    tk::ArgmaxArgs b = a;
+    b.in = in + r0 * stride;
+    b.row0 = 0;
+    b.span_slot = (uint64_t *)(base + off_slot);
+    b.row_done = (int32_t *)base;
+    b.out_idx = out_idx + r0;
+    b.out_val = out_val + r0;
+    b.out_count = out_count + r0;
+    b.out_nonfinite = out_nonfinite + r0;
+    if (tk::launch_argmax(b, nr, stream) != hipSuccess) {
+      result = TK_ERR_DEVICE;
+      break;
+    }
+  }
+  if (owned && hipFreeAsync(base, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  return result;
+}
+
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
               const tk_options *opt, int64_t col_base = 0, uint32_t inf = 0x7F80u) {
   tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
   if (st != TK_OK) return st;
   if (col_base < 0 || col_base > (int64_t)INT32_MAX - cols + (cols > 0 ? 1 : 0)) return TK_ERR_SHAPE;
-  int32_t forced = 0, exact = 0;
+  int32_t forced = 0, exact = 0, general = 0;
   if (opt) {
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (opt->reserved[i] != 0) return TK_ERR_OPTION;
     if (opt->exact != 0 && opt->exact != 1) return TK_ERR_OPTION;
+    if (opt->general != 0 && opt->general != 1) return TK_ERR_OPTION;
     exact = opt->exact;
+    general = opt->general;
     forced = opt->spans;
     if (forced < 0 || forced > kMaxSpans) return TK_ERR_OPTION;
     if (forced > 1 && cols > 0 && forced > cols) return TK_ERR_OPTION;
@@ -273,6 +385,12 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   hipStream_t stream = (hipStream_t)stream_handle;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  if (k == 1 && !general) {
+    const int32_t s1 = forced > 0 ? forced : plan_argmax(rows, cols, device_cus(dev));
+    if (s1 <= kMergeGroup)
+      return run_argmax(rows, cols, stride, in, out_idx, out_val, out_count, out_nonfinite, stream, dev, s1,
+                        col_base, inf);
+  }
   const int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
 
   tk::ScanArgs sa{};
@@ -403,9 +521,10 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
   if (st != TK_OK) return st;
   int32_t forced = 0, exact = 0;
   if (opt) {
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (opt->reserved[i] != 0) return TK_ERR_OPTION;
     if (opt->exact != 0 && opt->exact != 1) return TK_ERR_OPTION;
+    if (opt->general != 0 && opt->general != 1) return TK_ERR_OPTION;
     exact = opt->exact;
     forced = opt->spans;
     if (forced < 0 || forced > kMergeGroup) return TK_ERR_OPTION;
@@ -606,8 +725,12 @@ tk_status tk_sample_topk_bf16(int64_t rows, int32_t k, const int32_t *idx, const
 }
 
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
-  (void)k;
-  return plan(rows, cols, compute_units > 0 ? compute_units : 256);
+  const int32_t cus = compute_units > 0 ? compute_units : 256;
+  if (k == 1) {
+    const int32_t s1 = plan_argmax(rows, cols, cus);
+    if (s1 <= kMergeGroup) return s1;
+  }
+  return plan(rows, cols, cus);
 }
 
 int32_t tk_max_k(void) { return kMaxK; }

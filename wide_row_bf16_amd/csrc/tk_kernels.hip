@@ -153,17 +153,23 @@ struct Filter {
   uint32_t ftrip;  // trip when uint16(bits) >= ftrip: -inf / NaN patterns not flagged yet
 };
 
-__device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
-  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.kth) >> 16;
-  const uint32_t tkey = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
-  const uint32_t flags = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags);
+// The filter for threshold key tkey (wave-uniform), given the flags already
+// raised and the format's +inf pattern.
+__device__ __forceinline__ Filter filter_for(uint32_t tkey, uint32_t flags, uint32_t inf) {
   Filter f;
   f.nonneg = tkey >= 0x8000u;
   f.t16 = (int32_t)tkey - 0x8000;
   f.tu = 0x10000u - tkey;
-  const uint32_t ninf = 0x8000u | (uint32_t)__builtin_amdgcn_readfirstlane((int)w.inf);
+  const uint32_t ninf = 0x8000u | inf;
   f.ftrip = (flags & kNinf) ? ((flags & kNan) ? 0x10000u : ninf + 1u) : ninf;
   return f;
+}
+
+__device__ __forceinline__ Filter make_filter(const WaveTopK &w) {
+  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.kth) >> 16;
+  const uint32_t tkey = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
+  return filter_for(tkey, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)w.inf));
 }
 
 __device__ __forceinline__ v2i16 as_i16x2(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
@@ -264,15 +270,15 @@ __device__ __forceinline__ void take_lanes_value(WaveTopK &w, uint4 d, uint32_t 
 
 // Flags the -inf / NaN patterns at or above ftrip in the vectors of lanes
 // `lanes`; nothing is kept here (a -inf that can be kept also passes T).
-__device__ __forceinline__ void take_flags(WaveTopK &w, uint4 d, uint64_t lanes, uint32_t ftrip) {
+__device__ __forceinline__ void take_flags(uint32_t &flags, uint32_t inf, uint4 d, uint64_t lanes, uint32_t ftrip) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
     const uint64_t m = lanes_uge(b, ftrip) & lanes;
-    if (m & lanes_eq(b, 0x8000u | w.inf)) w.flags |= kNinf;
-    if (m & lanes_ugt(b, 0x8000u | w.inf)) w.flags |= kNan;
+    if (m & lanes_eq(b, 0x8000u | inf)) flags |= kNinf;
+    if (m & lanes_ugt(b, 0x8000u | inf)) flags |= kNan;
   }
 }
 
@@ -331,7 +337,7 @@ __device__ __forceinline__ void take_chunk(WaveTopK &w, const uint4 (&v)[kChunkV
         publish(w.tau, w.wave, w);
         w.ext = max(shared_bound(w.tau, w.wave), w.floor);
       } else {
-        if (mf) take_flags(w, d, mf, f0.ftrip);
+        if (mf) take_flags(w.flags, w.inf, d, mf, f0.ftrip);
         if (mv) {
           const Filter f = make_filter(w);
           if (f.nonneg) take_lanes_value<true>(w, d, inv0, mv, f);
@@ -695,6 +701,234 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k = 1: the row's best entry alone (greedy decoding takes this argmax).  The
+// same span split, loads and raw-bit filter as span_scan_kernel, with the
+// kept list reduced to one wave-uniform composite: T = max(the wave's best
+// key, the bound from the other waves' best keys), an element matters only if
+// its key exceeds T, and a tripped chunk costs one per-lane maximum of the
+// tripping vectors' composites and one wave-wide maximum.  No floors, no list
+// merges: a split row keeps one composite per span, and the row's last
+// workgroup takes the maximum of its S <= kMergeGroup span results.
+
+struct WaveArgmax {
+  uint32_t best;    // wave-uniform best in-wave composite (key << 16 | 0xFFFF - rel), 0 = none
+  uint32_t flags;   // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
+  uint32_t inf;     // +inf pattern of the input format
+  int wave;
+  uint32_t *s_key;  // LDS: best key published by each wave of the workgroup
+  Xchg x;
+};
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v, const Xchg &x) {
+  v = max(v, partner<1>(v, x));
+  v = max(v, partner<2>(v, x));
+  v = max(v, partner<4>(v, x));
+  v = max(v, partner<8>(v, x));
+  v = max(v, partner<16>(v, x));
+  v = max(v, partner<32>(v, x));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v, const Xchg &x) {
+  uint64_t y;
+  y = partner64<1>(v, x); v = v > y ? v : y;
+  y = partner64<2>(v, x); v = v > y ? v : y;
+  y = partner64<4>(v, x); v = v > y ? v : y;
+  y = partner64<8>(v, x); v = v > y ? v : y;
+  y = partner64<16>(v, x); v = v > y ? v : y;
+  y = partner64<32>(v, x); v = v > y ? v : y;
+  return v;
+}
+
+// Keys at or below this bound lose to another wave's best: to a wave on the
+// left (lower columns) also on equal keys, to a wave on the right only on
+// lower ones.  Published keys only rise, so a stale read is still a bound.
+__device__ __forceinline__ uint32_t argmax_bound(const WaveArgmax &w) {
+  uint32_t ext = 0;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    if (o == w.wave) continue;
+    const uint32_t t = __hip_atomic_load(&w.s_key[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ext = max(ext, o < w.wave ? t : (t > 0 ? t - 1 : 0u));
+  }
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ext);
+}
+
+// This lane's best composite among the eight elements of d (element e at
+// 0xFFFF - rel = inv0 - e); NaN gives 0 and sets nan.  On equal keys the
+// lower column has the larger composite.  (Positive NaN patterns reach this
+// path through the value trip, whose int16 test they always pass; the flag
+// trip only sees patterns from -inf upwards as uint16.)
+__device__ __forceinline__ uint32_t vector_best(uint4 d, uint32_t inv0, uint32_t inf, bool &nan) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+    const uint32_t key = order_key(b, inf);
+    nan |= key == 0;
+    m = max(m, key ? (key << 16) | (inv0 - (uint32_t)e) : 0u);
+  }
+  return m;
+}
+
+// One chunk (as take_chunk): trip bits against T at the chunk start, then the
+// tripping lanes' vector maxima and one wave maximum.
+__device__ __forceinline__ void argmax_chunk(WaveArgmax &w, const uint4 (&v)[kChunkVecs], uint32_t first,
+                                             uint32_t nvec, int64_t col_first, int64_t base) {
+  const Filter f = filter_for(max(w.best >> 16, argmax_bound(w)), w.flags, w.inf);
+  uint64_t vt[kChunkVecs], ft[kChunkVecs];
+  lane_trips<kChunkVecs>(v, f, vt, ft);
+  uint64_t any_v = 0, any_f = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint64_t valid = lanes_ult(first + (uint32_t)(u * kWave + lane_id()), nvec);
+    vt[u] &= valid;
+    ft[u] &= valid;
+    any_v |= vt[u];
+    any_f |= ft[u];
+  }
+  if (any_f) {
+#pragma unroll
+    for (int u = 0; u < kChunkVecs; ++u)
+      if (ft[u]) take_flags(w.flags, w.inf, v[u], ft[u], f.ftrip);
+  }
+  if (!any_v) return;
+  const uint32_t l = (uint32_t)lane_id();
+  const uint32_t inv0 = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
+  uint32_t m = 0;
+  bool nan = false;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u)
+    if ((vt[u] >> l) & 1u) m = max(m, vector_best(v[u], inv0 - (uint32_t)(u * kWave * kVecElems), w.inf, nan));
+  if (ballot(nan)) w.flags |= kNan;
+  const uint32_t best = max(w.best, wave_max(m, w.x));
+  if (best != w.best) {
+    w.best = best;
+    if (l == 0) __hip_atomic_store(&w.s_key[w.wave], best >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Columns [lo, hi) one per lane (row edges, tiny spans): every element.
+__device__ void argmax_columns(WaveArgmax &w, const uint16_t *row, int64_t lo, int64_t hi, int64_t base) {
+  uint32_t m = 0;
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? (uint32_t)row[col] : 0u;
+    const uint32_t key = valid ? order_key(b, w.inf) : 0u;
+    if (ballot(valid && (b & 0x7FFFu) > w.inf)) w.flags |= kNan;
+    if (ballot(valid && b == (0x8000u | w.inf))) w.flags |= kNinf;
+    m = max(m, key ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u);
+  }
+  w.best = max(w.best, wave_max(m, w.x));
+}
+
+__global__ __launch_bounds__(kWgThreads) void argmax_scan_kernel(ArgmaxArgs a) {
+  __shared__ uint32_t s_key[kWgWaves];
+  __shared__ uint64_t s_best[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const uint16_t *row = a.in + r * a.stride;
+
+  // the span and wave shares of span_scan_kernel
+  const int64_t a0 = (int64_t)((8u - (uint32_t)(((uintptr_t)row >> 1) & 7u)) & 7u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kVecElems : 0;
+  int64_t j0 = 0, j1 = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kVecElems * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+  const int64_t base = (wave == 0 && head_hi > 0) ? 0 : a0 + kVecElems * wv0;
+
+  if (threadIdx.x < kWgWaves) s_key[threadIdx.x] = 0;
+  __syncthreads();
+  WaveArgmax w;
+  w.best = 0;
+  w.flags = 0;
+  w.inf = a.inf;
+  w.wave = wave;
+  w.s_key = s_key;
+  w.x = make_xchg();
+
+  if (wave == 0 && head_hi > 0) argmax_columns(w, row, 0, head_hi, base);
+  const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t nvec = (uint32_t)(wv1 - wv0);
+  if (nvec > 0) {
+    constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+    const uint32_t lane_off = (uint32_t)l * 16u;
+    const int64_t col_first = a0 + kVecElems * wv0;
+    uint4 A[kChunkVecs], B[kChunkVecs];
+    load_chunk(A, vp, nvec, 0, lane_off);
+    for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+      load_chunk(B, vp, nvec, first + kStep, lane_off);
+      argmax_chunk(w, A, first, nvec, col_first, base);
+      if (first + kStep >= nvec) break;
+      load_chunk(A, vp, nvec, first + 2 * kStep, lane_off);
+      argmax_chunk(w, B, first + kStep, nvec, col_first, base);
+    }
+  }
+  if (wave == kWgWaves - 1 && tail_hi > tail_lo) argmax_columns(w, row, tail_lo, tail_hi, base);
+
+  if (l == 0) {
+    s_best[wave] = composite64(w.best, base);
+    s_fl[wave] = w.flags;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  uint64_t best = 0;
+  uint32_t fl = 0;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    best = best > s_best[o] ? best : s_best[o];
+    fl |= s_fl[o];
+  }
+  if (S > 1) {
+    // span result to its slot (flags in bits 48..50), then the arrival count;
+    // the last workgroup of the row takes the maximum of all slots
+    const int64_t rb = r - a.row0;
+    if (l == 0) __hip_atomic_store(&a.span_slot[rb * S + s], best | ((uint64_t)fl << 48), __ATOMIC_RELAXED, kAgent);
+    __builtin_amdgcn_s_waitcnt(0);
+    int last = 0;
+    if (l == 0) last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
+    if (!ballot(last)) return;
+    const uint64_t v = l < S ? __hip_atomic_load(&a.span_slot[rb * S + l], __ATOMIC_RELAXED, kAgent) : 0;
+    const uint32_t f = (uint32_t)(v >> 48);
+    fl = (ballot(f & kNan) ? kNan : 0u) | (ballot(f & kNinf) ? kNinf : 0u);
+    best = wave_max64(v & 0x0000FFFFFFFFFFFFull, make_xchg());
+    if (l == 0) __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
+  }
+  if (l == 0) {
+    if ((uint32_t)(best >> 32) == 0x8000u + a.inf) fl |= kPinf;
+    if (best) {
+      a.out_idx[r] = (int32_t)(col_of(best) + a.col_base);
+      a.out_val[r] = value_bits(best, row);
+    } else {
+      a.out_idx[r] = TK_FILL_IDX;
+      a.out_val[r] = (uint16_t)TK_FILL_VAL;
+    }
+    a.out_count[r] = best ? 1 : 0;
+    a.out_nonfinite[r] = fl;
+  }
+}
+
 // Folds up to kMergeGroup sorted candidate lists of one row into one.  All
 // threads first stage the group's lists in LDS (every load in flight at
 // once), then each wave folds its share pairwise in registers (lane j holds
@@ -861,6 +1095,12 @@ hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream) {
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream) {
   const int64_t blocks = rows_in_launch * a.spans;
   hipLaunchKernelGGL(span_scan_kernel, dim3((uint32_t)blocks), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const ArgmaxArgs &a, int64_t rows_in_launch, hipStream_t stream) {
+  if (rows_in_launch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_scan_kernel, dim3((uint32_t)(rows_in_launch * a.spans)), dim3(kWgThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -34,6 +34,29 @@ struct ScanArgs {
   uint32_t inf;         // +inf bit pattern of the input format: 0x7F80 bf16, 0x7C00 fp16
 };
 
+// k = 1 (argmax) scan, one workgroup per (row, span) as ScanArgs.  With
+// spans == 1 it writes the outputs; with 2 <= spans <= kMergeGroup each
+// workgroup writes its span's best composite (key << 32 | ~col, flags in bits
+// 48..50) to span_slot and the row's last workgroup (row_done, as ScanArgs)
+// writes the outputs.
+struct ArgmaxArgs {
+  const uint16_t *in;
+  int64_t row0;
+  int64_t cols;
+  int64_t stride;
+  int32_t spans;
+  uint32_t inf;         // +inf bit pattern of the input format
+  int64_t col_base;     // added to the output column index
+  uint64_t *span_slot;  // [rows_in_launch][spans]
+  int32_t *row_done;    // per-row arrival counters, zero between calls
+  int32_t *out_idx;
+  uint16_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+};
+
+hipError_t launch_argmax(const ArgmaxArgs &a, int64_t rows_in_launch, hipStream_t stream);
+
 // One merge workgroup per (row, group of up to kMergeGroup input lists).
 // With lists_out == 1 the merge writes the final outputs.
 struct MergeArgs {
