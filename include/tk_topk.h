@@ -37,6 +37,12 @@
  * them), and the buffer's per-row merge counters return to zero at the end of
  * every call.
  *
+ * k up to 64 keeps one wavefront lane per entry; 64 < k <= TK_MAX_K (256)
+ * runs a scan whose per-wave kept list spans two or four registers (bf16 and
+ * fp16 rows; the pages give the library a compile-time max_k, and this is
+ * its extension).  fp32 rows, the shard merge and sampling take k <=
+ * TK_MAX_K_LANE (64).
+ *
  * Errors: the guards below run on the host before any device work; on a
  * guard error nothing is launched and nothing is written.  TK_ERR_DEVICE
  * reports a failed allocation or launch; an asynchronous fault surfaces at the
@@ -51,7 +57,8 @@
 extern "C" {
 #endif
 
-#define TK_MAX_K 64u /* largest k; one wavefront lane per kept entry */
+#define TK_MAX_K 256u     /* largest k of tk_topk_bf16 / tk_topk_f16 (and their _ex, _shard forms) */
+#define TK_MAX_K_LANE 64u /* largest k of fp32 rows, the shard merge and sampling: one lane per entry */
 
 #define TK_NONFINITE_NAN 1u    /* the row has at least one NaN (none is an entry)  */
 #define TK_NONFINITE_POSINF 2u /* the row has at least one +inf                    */
@@ -64,7 +71,7 @@ typedef enum tk_status {
   TK_OK = 0,
   TK_ERR_NULL = 1,   /* a required pointer is NULL: with rows > 0 every output, and `in` when cols > 0 */
   TK_ERR_SHAPE = 2,  /* rows < 0, cols < 0, cols > INT32_MAX, row_stride < cols, or sizes overflow */
-  TK_ERR_K = 3,      /* k < 1 or k > TK_MAX_K */
+  TK_ERR_K = 3,      /* k < 1 or k above the entry point's limit (TK_MAX_K or TK_MAX_K_LANE) */
   TK_ERR_ALIGN = 4,  /* in/out_val not 2-byte aligned, or out_idx/out_count/out_nonfinite not 4-byte aligned */
   TK_ERR_ALIAS = 5,  /* two of the five buffers overlap (outputs must not alias the input or each other) */
   TK_ERR_DEVICE = 6, /* HIP reported an error while allocating or launching */
@@ -91,7 +98,10 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
  *          candidate lists are merged in the same order: by the row's last
  *          scan workgroup for n <= 64, by merge dispatches above.  Rejected with
  *          TK_ERR_OPTION when a span would exceed the library's span limit
- *          (tk_max_span_cols()) or n > cols (for cols > 0).
+ *          (tk_max_span_cols()) or n > cols (for cols > 0), and for k > 64
+ *          when n > 64 (k > 64 splits a row into at most 64 spans, so rows
+ *          wider than 64 x tk_max_span_cols() give TK_ERR_SHAPE there).
+ *          The automatic plan splits k > 64 rows into at most 8 spans.
  *   exact  0 = automatic; 1 = never take the speculative floor (wide spans
  *          otherwise skip elements below a floor estimated from a sample and
  *          verify it afterwards, scanning again when it does not hold).
@@ -133,7 +143,8 @@ tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
  * aligned, row_stride in elements; out_val: uint32 [rows][k], the entries'
  * own bits, empty slots 0x7FC00000.  Keys are 32 bits wide and composites 64,
  * so one span may be any width; tk_options.spans accepts 0..64
- * (TK_ERR_OPTION above).  tk_validate_f32 gives the guards alone.
+ * (TK_ERR_OPTION above).  1 <= k <= TK_MAX_K_LANE (TK_ERR_K above).
+ * tk_validate_f32 gives the guards alone.
  */
 tk_status tk_topk_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
                       int32_t *out_idx, uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream);
@@ -155,7 +166,8 @@ tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32
 /*
  * The span count the automatic plan picks for a shape on a GPU with
  * `compute_units` CUs (host-only arithmetic; no HIP call).  For k == 1 that
- * is the plan of the argmax scan (bf16 and fp16 rows).
+ * is the plan of the argmax scan, for k > 64 that of the multi-register scan
+ * (bf16 and fp16 rows).
  */
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units);
 
@@ -188,7 +200,8 @@ tk_status tk_topk_bf16_shard(int64_t rows, int64_t cols, int64_t row_stride, int
  *   count_in, mask_in  [shards][rows]      per-shard counts and non-finite masks
  * Outputs as tk_topk_bf16: count = min(k, sum of the shard counts), mask = OR
  * of the shard masks, entries in order, fill after count.  Every shard must
- * have used this k.  1 <= shards <= TK_MAX_SHARDS (else TK_ERR_SHAPE).
+ * have used this k, 1 <= k <= TK_MAX_K_LANE (else TK_ERR_K).
+ * 1 <= shards <= TK_MAX_SHARDS (else TK_ERR_SHAPE).
  * Guards as tk_topk_bf16 (NULL, alignment, outputs overlapping each other or
  * an input -> TK_ERR_ALIAS); entries are trusted as written by
  * tk_topk_bf16_shard (no memory is addressed through them).  Asynchronous on
@@ -233,7 +246,7 @@ tk_status tk_validate_merge_bf16(int64_t rows, int32_t shards, int32_t k, const 
  *     idx[kept - 1].
  * Outputs: out_token, out_kept int32 [rows].  `offset` is the decode step:
  * the same (seed, offset, row) always draws the same u.  Guards: 1 <= k <=
- * TK_MAX_K (TK_ERR_K), 0 <= temperature finite and 0 < top_p <= 1
+ * TK_MAX_K_LANE (TK_ERR_K), 0 <= temperature finite and 0 < top_p <= 1
  * (TK_ERR_OPTION), NULL, alignment, outputs overlapping each other or an
  * input (TK_ERR_ALIAS).  Asynchronous on `stream`; no scratch memory.
  */

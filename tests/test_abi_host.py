@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_constants():
     text = open(HEADER).read()
-    assert tk.max_k() == int(re.search(r"#define TK_MAX_K (\d+)u", text).group(1)) == 64
+    assert tk.max_k() == int(re.search(r"#define TK_MAX_K (\d+)u", text).group(1)) == 256
+    assert int(re.search(r"#define TK_MAX_K_LANE (\d+)u", text).group(1)) == 64
     assert tk.max_span_cols() >= 4 * 65000
     assert b"gfx950" in tk.load().tk_build_info()
     for s in range(8):
@@ -51,8 +52,8 @@ def test_guard_accepts_valid_calls():
     assert v(rows=0, i=None, o=None, val=None, c=None, m=None) == OK  # empty: nothing is touched
     assert v(cols=0, stride=0) == OK
     assert v(cols=0, stride=0, i=None) == OK  # nothing of the input is read
-    assert v(k=64) == OK and v(k=1) == OK
-    assert v(k=64, cols=3, stride=3) == OK  # k may exceed cols
+    assert v(k=64) == OK and v(k=1) == OK and v(k=65) == OK and v(k=256) == OK
+    assert v(k=64, cols=3, stride=3) == OK and v(k=256, cols=3, stride=3) == OK  # k may exceed cols
     assert v(i=IN + 2, val=VAL + 2) == OK    # 2-byte alignment is enough for bf16 buffers
 
 
@@ -65,7 +66,7 @@ def test_guard_accepts_valid_calls():
         (dict(stride=99), SHAPE),
         (dict(rows=2**40, stride=2**40), SHAPE),
         (dict(k=0), K),
-        (dict(k=65), K),
+        (dict(k=257), K),
         (dict(k=-3), K),
         (dict(i=None), NULL),
         (dict(o=None), NULL),
@@ -123,6 +124,18 @@ def test_plan_k1():
             assert rows < 256 or s == max(1, -(-(cols // 8) // 32640))  # only the span width limit
 
 
+def test_plan_large_k():
+    # k > 64: the k <= 64 plan, at most 8 spans unless the span width needs more
+    assert tk.plan_spans(1024, 151936, 128) == 1
+    assert tk.plan_spans(15, 98592, 256) == 8
+    assert tk.plan_spans(64, 151936, 100) == 4
+    assert tk.plan_spans(2, 10**7, 65) == (10**7 // 8 + 32639) // 32640
+    for rows in (1, 15, 64, 256, 1000):
+        for cols in (1, 4096, 70000, 248320, 600000):
+            s = tk.plan_spans(rows, cols, 200)
+            assert 1 <= s <= max(8, -(-(cols // 8) // 32640)) and s <= tk.plan_spans(rows, cols, 64)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f16", "f32"])
 def test_option_fields(fmt):
     """tk_options: exact and general take 0 or 1, the reserved words must be
@@ -141,6 +154,15 @@ def test_option_fields(fmt):
     assert ctypes.sizeof(tk.TkOptions) == 32
     assert call() == OK and call(general=1) == OK and call(exact=1, general=1, spans=4) == OK
     assert call(general=2) == OPTION and call(general=-1) == OPTION and call(exact=2) == OPTION
+    if fmt != "f32":
+        # k > 64: at most 64 spans, forced or needed by the width
+        def wide(spans, cols):
+            return fn(0, cols, cols, 65, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(tk.TkOptions(spans=spans)))
+
+        assert wide(64, 100000) == OK and wide(65, 100000) == OPTION
+        assert wide(0, 64 * 261120) == OK and wide(0, 64 * 261120 + 8) == SHAPE
+        assert tk.validate(1, 64 * 261120 + 8, 64 * 261120 + 8, 65, IN, IDX, VAL, CNT, MSK) == SHAPE
+        assert tk.validate(1, 64 * 261120 + 8, 64 * 261120 + 8, 64, IN, IDX, VAL, CNT, MSK) == OK
     for i in range(5):
         assert call(reserved={i: 1}) == OPTION
 
@@ -219,6 +241,7 @@ def test_f32_guards():
     assert v32(i=IN + 2) == ALIGN and v32(val=VAL + 2) == ALIGN  # 4-byte elements
     assert v32(i=IN + 4) == OK
     assert v32(k=0) == K and v32(stride=99) == SHAPE
+    assert v32(k=64) == OK and v32(k=65) == K  # fp32 rows keep one lane per entry
     # the input spans 4 bytes per element: an output 1000 bytes in overlaps it
     assert v32(idx=IN + 1000) == ALIAS
     assert tk.validate(3, 100, 100, 8, IN, IN + 1000, VAL, CNT, MSK) == OK  # bf16: 600 bytes of input only

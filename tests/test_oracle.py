@@ -33,6 +33,15 @@ def test_library_sorts(oracle_lib):
     pin_library_sorts(oracle_lib)
 
 
+def test_library_sorts_large_k(oracle_lib):
+    # k beyond one wavefront (65..256): the same definition, pinned the same way
+    pin_library_sorts(oracle_lib, widths=(1, 64, 65, 257, 300, 1000), ks=(65, 128, 200, 256), seed=5)
+
+
+def test_invariants_large_k(oracle_lib):
+    pin_invariants(oracle_lib, widths=(4096, 9000), ks=(65, 129, 256), seed=9)
+
+
 def test_padding_never_read(oracle_lib):
     pin_padding(oracle_lib)
 

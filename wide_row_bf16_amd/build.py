@@ -15,7 +15,8 @@ LIBRARY = os.path.join(PKG, "libtk_topk.so")
 ARCH = os.environ.get("TK_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "tk_kernels.hip"), os.path.join(CSRC, "tk_sample.hip"), os.path.join(CSRC, "tk_f32.hip"), os.path.join(CSRC, "tk_api.cpp")]
+SOURCES = [os.path.join(CSRC, "tk_kernels.hip"), os.path.join(CSRC, "tk_sample.hip"), os.path.join(CSRC, "tk_f32.hip"),
+           os.path.join(CSRC, "tk_wide.hip"), os.path.join(CSRC, "tk_api.cpp")]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -18,6 +18,7 @@
 namespace {
 
 using tk::kMaxK;
+using tk::kMaxKWide;
 using tk::kMaxSpanVecs;
 using tk::kMergeGroup;
 using tk::kFusedMaxRows;
@@ -44,9 +45,12 @@ bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.h
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
 tk_status guard(int64_t rows, int64_t cols, int64_t stride, int32_t k, const void *in, const void *out_idx,
-                const void *out_val, const void *out_count, const void *out_nonfinite, int eb = 2) {
+                const void *out_val, const void *out_count, const void *out_nonfinite, int eb = 2,
+                int32_t kmax = kMaxKWide) {
   if (rows < 0 || cols < 0 || cols > INT32_MAX || stride < cols) return TK_ERR_SHAPE;
-  if (k < 1 || k > kMaxK) return TK_ERR_K;
+  if (k < 1 || k > kmax) return TK_ERR_K;
+  // k > 64 splits a row into at most kMergeGroup spans of kMaxSpanVecs vectors
+  if (k > kMaxK && (cols / kVecElems + kMaxSpanVecs - 1) / kMaxSpanVecs > kMergeGroup) return TK_ERR_SHAPE;
   if (rows == 0) return TK_OK;
   if ((cols > 0 && !in) || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;
   const int64_t big = std::numeric_limits<int64_t>::max() / 8;
@@ -361,6 +365,86 @@ tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t 
   return result;
 }
 
+// 64 < k <= 256: the multi-register scan (tk_wide.hip).  Automatic plans
+// split as for k <= 64 but into at most kWideMaxAutoSpans spans (the fold of
+// a split row merges lists of up to 256 entries); forced plans take up to
+// kMergeGroup spans; rows needing more spans (over 16.7 M columns) are
+// rejected with TK_ERR_SHAPE.  Split rows are always folded by their last
+// workgroup: scratch = the arrival counters, then [batch][S][k] composites,
+// [batch][S] counts and flags.
+constexpr int32_t kWideMaxAutoSpans = 8;
+
+int32_t plan_wide(int64_t rows, int64_t cols, int32_t compute_units) {
+  int32_t spans = plan(rows, cols, compute_units);
+  if (spans > kWideMaxAutoSpans) spans = kWideMaxAutoSpans;
+  if (spans < (int32_t)min_spans(cols)) spans = (int32_t)min_spans(cols);
+  return spans;
+}
+
+tk_status run_wide(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
+                   uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, hipStream_t stream, int dev,
+                   int32_t forced, int32_t exact, int64_t col_base, uint32_t inf) {
+  const int32_t spans = forced > 0 ? forced : plan_wide(rows, cols, device_cus(dev));
+  if (spans > kMergeGroup) return TK_ERR_SHAPE;  // excluded by the guards; kept as a bound on the fold
+  tk::ScanArgs sa{};
+  sa.in = in;
+  sa.cols = cols;
+  sa.stride = stride;
+  sa.k = k;
+  sa.spans = spans;
+  sa.exact = exact;
+  sa.spec_rank = exact ? 0 : spec_rank(k, cols / spans);
+  sa.out_idx = out_idx;
+  sa.out_val = out_val;
+  sa.out_count = out_count;
+  sa.out_nonfinite = out_nonfinite;
+  sa.col_base = col_base;
+  sa.inf = inf;
+  const int64_t rows_per_launch = kMaxBlocksPerLaunch / spans;
+  if (spans == 1) {
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+      const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+      sa.row0 = r0;
+      if (tk::launch_wide_scan(sa, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
+    }
+    return TK_OK;
+  }
+  const int64_t batch_cap = rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
+  const int64_t batch = rows < batch_cap ? rows : batch_cap;
+  const size_t nlists = (size_t)batch * (size_t)spans;
+  const size_t off_list = align256((size_t)kFusedMaxRows * sizeof(int32_t));
+  const size_t off_count = align256(off_list + nlists * (size_t)k * sizeof(uint64_t));
+  const size_t off_flags = align256(off_count + nlists * sizeof(int32_t));
+  const size_t total = align256(off_flags + nlists * sizeof(uint32_t));
+  keep_pool(dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  char *base = nullptr;
+  bool owned = false;
+  const tk_status sst = acquire_scratch(dev, stream, total, &base, &owned);
+  if (sst != TK_OK) return sst;
+  tk_status result = TK_OK;
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    tk::ScanArgs b = sa;
+    b.in = in + r0 * stride;
+    b.row0 = 0;
+    b.span_list = (uint64_t *)(base + off_list);
+    b.span_count = (int32_t *)(base + off_count);
+    b.span_flags = (uint32_t *)(base + off_flags);
+    b.row_done = (int32_t *)base;
+    b.out_idx = out_idx + r0 * k;
+    b.out_val = out_val + r0 * k;
+    b.out_count = out_count + r0;
+    b.out_nonfinite = out_nonfinite + r0;
+    if (tk::launch_wide_scan(b, nr, stream) != hipSuccess) {
+      result = TK_ERR_DEVICE;
+      break;
+    }
+  }
+  if (owned && hipFreeAsync(base, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  return result;
+}
+
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
               const tk_options *opt, int64_t col_base = 0, uint32_t inf = 0x7F80u) {
@@ -379,12 +463,16 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
     if (forced < 0 || forced > kMaxSpans) return TK_ERR_OPTION;
     if (forced > 1 && cols > 0 && forced > cols) return TK_ERR_OPTION;
     if (forced >= 1 && forced < min_spans(cols)) return TK_ERR_OPTION;
+    if (k > kMaxK && forced > kMergeGroup) return TK_ERR_OPTION;
   }
   if (rows == 0) return TK_OK;
 
   hipStream_t stream = (hipStream_t)stream_handle;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  if (k > kMaxK)
+    return run_wide(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, dev, forced,
+                    exact, col_base, inf);
   if (k == 1 && !general) {
     const int32_t s1 = forced > 0 ? forced : plan_argmax(rows, cols, device_cus(dev));
     if (s1 <= kMergeGroup)
@@ -517,7 +605,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
 tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint32_t *in, int32_t *out_idx,
                 uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
                 const tk_options *opt) {
-  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4);
+  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxK);
   if (st != TK_OK) return st;
   int32_t forced = 0, exact = 0;
   if (opt) {
@@ -645,7 +733,7 @@ tk_status tk_topk_f32_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
 tk_status tk_validate_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
                           const int32_t *out_idx, const uint32_t *out_val, const int32_t *out_count,
                           const uint32_t *out_nonfinite) {
-  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4);
+  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxK);
 }
 
 tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
@@ -726,6 +814,7 @@ tk_status tk_sample_topk_bf16(int64_t rows, int32_t k, const int32_t *idx, const
 
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
   const int32_t cus = compute_units > 0 ? compute_units : 256;
+  if (k > kMaxK) return plan_wide(rows, cols, cus);
   if (k == 1) {
     const int32_t s1 = plan_argmax(rows, cols, cus);
     if (s1 <= kMergeGroup) return s1;
@@ -733,7 +822,7 @@ int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_uni
   return plan(rows, cols, cus);
 }
 
-int32_t tk_max_k(void) { return kMaxK; }
+int32_t tk_max_k(void) { return kMaxKWide; }
 
 int64_t tk_max_span_cols(void) { return tk::kMaxSpanCols; }
 
@@ -742,7 +831,7 @@ const char *tk_status_string(tk_status s) {
     case TK_OK: return "ok";
     case TK_ERR_NULL: return "a required pointer is NULL";
     case TK_ERR_SHAPE: return "invalid shape (rows, cols or row_stride)";
-    case TK_ERR_K: return "k out of range [1, TK_MAX_K]";
+    case TK_ERR_K: return "k out of range [1, TK_MAX_K] ([1, TK_MAX_K_LANE] for fp32 rows, shard merge, sampling)";
     case TK_ERR_ALIGN: return "misaligned buffer";
     case TK_ERR_ALIAS: return "buffers overlap";
     case TK_ERR_DEVICE: return "HIP error while allocating or launching";

@@ -13,7 +13,8 @@ namespace tk {
 constexpr int kWave = 64;                      // CDNA wavefront width
 constexpr int kWgWaves = 4;                    // waves per scan workgroup
 constexpr int kWgThreads = kWave * kWgWaves;   // 256
-constexpr int kMaxK = 64;                      // kept entries: one per lane
+constexpr int kMaxK = 64;                      // kept entries of the one-register scans: one per lane
+constexpr int kMaxKWide = 256;                 // k of the multi-register scan (four registers per wave)
 constexpr int kVecElems = 8;                   // bf16 per 16-byte load
 constexpr int kChunkVecs = 4;                  // 16-byte loads per lane per chunk
 constexpr int64_t kMaxWaveCols = 65536;        // a wave's relative column fits 16 bits
@@ -27,7 +28,9 @@ constexpr int kSpecChunks = 16;                // chunks per wave before a specu
 constexpr int kSampleElems = kWgWaves * kChunkVecs * kWave * kVecElems;  // pooled sample: each wave's first chunk
 constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
 
-static_assert(kMaxK == (int)TK_MAX_K, "public and internal max k differ");
+static_assert(kMaxKWide == (int)TK_MAX_K, "public and internal max k differ");
+static_assert(kMaxK == (int)TK_MAX_K_LANE, "public and internal lane max k differ");
+static_assert(kMaxKWide == 4 * kWave, "the multi-register scan keeps at most four registers");
 static_assert(kMaxK <= kWave, "a wave holds one kept entry per lane");
 static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
 // A wave scans at most ceil(kMaxSpanVecs / kWgWaves) vectors plus two partial

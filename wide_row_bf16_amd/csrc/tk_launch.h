@@ -119,6 +119,11 @@ hipError_t launch_sample(const SampleArgs &a, hipStream_t stream);
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
 
+// 64 < k <= 256 (tk_wide.hip): ScanArgs as for launch_span_scan, with every
+// split row (2 <= spans <= kMergeGroup) folded by its last workgroup
+// (row_done, span_list [rows][spans][k], span_count, span_flags required then).
+hipError_t launch_wide_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream);
+
 // The fp32 scan (tk_f32.hip): as ScanArgs with 32-bit inputs and entry
 // values; split rows (2 <= spans <= kMergeGroup) are always folded by their
 // last workgroup (row_done required then).

@@ -1,0 +1,579 @@
+// Exact row-wise top-k for 64 < k <= 256 over bf16 and fp16 rows (gfx950).
+//
+// The operation and its order are those of the k <= 64 scan (TensorFold PR
+// #713, change 3: highest score first, the lower column on equal scores, one
+// answer whatever the split; the same order key, NaN policy and flags); only
+// the kept set is larger than a wavefront.  The pages give the library a
+// compile-time max_k; this file is what lets it exceed the lane count.
+//
+// Kept set.  A wave keeps its 64 R best composites in R VGPRs (R = 2 for
+// k <= 128, 4 for k <= 256): register j, lane i holds rank 64 j + i of the
+// concatenated descending list.
+//  - One insertion shifts every register right by one lane (DPP wave_shr),
+//    register j's lane 0 taking register j - 1's lane 63, and keeps
+//    max(entry, min(shifted, c)) -- the one-register rule applied to the
+//    whole list at once.
+//  - A batch of 64 is sorted and cascaded down the registers: against
+//    register j, the lane-wise max of the register and the reversed batch is
+//    the top 64 of both (a bitonic sequence, sorted in six stages) and stays;
+//    the lane-wise min, sorted likewise, is carried to register j + 1.
+//    Registers whose last entry already beats the batch's first are skipped.
+// The filter, the trip masks, the chunk loads and the flags are those of the
+// k <= 64 scan.  The exact floor is the k-th largest of the 256 lane maxima
+// of each wave's first chunk (k lanes hold an element at or above it); a
+// speculative floor (a lower rank of the same sample, verified after the scan
+// and followed by a rescan under the exact floor when it fails) spares most of
+// the insertions on wide spans.  The four wave lists meet in LDS by rank
+// (binary search in the other lists); split rows are folded by their last
+// workgroup with 64-bit list merges.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tk_config.h"
+#include "tk_launch.h"
+
+namespace tk {
+namespace {
+
+#include "tk_wave.h"
+#include "tk_scan16.h"
+
+// A speculative floor is tried only when each wave's share spans at least this
+// many chunks (shorter shares are mostly sample already).
+constexpr int kWideSpecChunks = 4;
+// This many tripping lanes in a vector take the dense path (all composites,
+// a per-lane sort, batch merges); fewer take the per-element lean path.
+constexpr int kWideDenseLanes = 16;
+
+// ---- R-register lists (32-bit in-wave composites) ----
+
+template <int R>
+__device__ __forceinline__ void wide_insert_one(uint32_t (&L)[R], uint32_t c) {
+  uint32_t carry[R];
+  carry[0] = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 1; j < R; ++j) carry[j] = readlane(L[j - 1], kWave - 1);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)carry[j], (int)L[j], 0x138, 0xF, 0xF, false);
+    L[j] = max(L[j], min(prev, c));
+  }
+}
+
+// Merges 64 candidates v (any order, 0 = none) into the list.
+template <int R>
+__device__ __forceinline__ void wide_merge_batch(uint32_t (&L)[R], uint32_t v, const Xchg &x) {
+  v = sort64_desc(v, x);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (!ballot(v != 0)) break;
+    // the batch's best does not beat this register's last entry: it passes on whole
+    if (readlane(v, 0) <= readlane(L[j], kWave - 1)) continue;
+    const uint32_t rv = partner<63>(v, x);
+    const uint32_t hi = max(L[j], rv), lo = min(L[j], rv);
+    L[j] = bitonic_merge64_desc(hi, x);
+    if (j + 1 < R) v = bitonic_merge64_desc(lo, x);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ uint32_t wide_at(const uint32_t (&L)[R], int rank) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if ((rank >> 6) == j) v = readlane(L[j], rank & (kWave - 1));
+  return v;
+}
+
+template <int R>
+struct WaveWide {
+  uint32_t L[R];
+  uint32_t kth;    // wave-uniform copy of rank k - 1
+  uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of other waves (or the floor)
+  uint32_t floor;  // wave-uniform floor: only keys > floor are kept
+  uint32_t flags;  // wave-uniform TK_NONFINITE_NAN / _NEGINF seen so far
+  uint32_t inf;
+  int km1;         // k - 1
+  int qm1;         // ceil(k / 4) - 1 (< 64)
+  int wave;
+  uint32_t *tau;   // LDS: [k-th key of each wave][ceil(k/4)-th key of each wave]
+  Xchg x;
+};
+
+// Candidates c of lanes m, each beating the k-th: one batch when many, else
+// one insertion each (a stale k-th only lets extra candidates through, which
+// changes ranks >= k only).
+template <int R>
+__device__ __forceinline__ void wide_offer(WaveWide<R> &w, uint32_t c, uint64_t m) {
+  if (__popcll(m) >= kBatchInsert) {
+    wide_merge_batch<R>(w.L, c > w.kth ? c : 0u, w.x);
+  } else {
+    do {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      wide_insert_one<R>(w.L, readlane(c, l));
+    } while (m);
+  }
+  w.kth = wide_at<R>(w.L, w.km1);
+}
+
+// The threshold sharing of the k <= 64 scan: a wave's k-th key bounds the
+// others (on equal keys the left wave wins), and the smallest ceil(k/4)-th
+// key of the four bounds every wave (k entries of the workgroup beat what is
+// below it).
+__device__ __forceinline__ uint32_t wide_bound(const uint32_t *s_tau, int wave) {
+  uint32_t ext = 0, qmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    const uint32_t t = __hip_atomic_load(&s_tau[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t q = __hip_atomic_load(&s_tau[kWgWaves + o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t b = o < wave ? t : (t > 0 ? t - 1 : 0u);
+    if (o != wave) ext = max(ext, b);
+    qmin = min(qmin, q);
+  }
+  if (qmin > 0) ext = max(ext, qmin - 1);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ext);
+}
+
+template <int R>
+__device__ __forceinline__ void wide_publish(WaveWide<R> &w) {
+  const uint32_t q = readlane(w.L[0], w.qm1) >> 16;
+  if (lane_id() == 0) {
+    __hip_atomic_store(&w.tau[w.wave], w.kth >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&w.tau[kWgWaves + w.wave], q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Few tripping lanes: the eight per-element tests against T on the raw bits
+// (lanes `valid`), then, for each element position with hits, the composites
+// of all lanes at once and one insertion per hit (the lean path of the k <= 64
+// scan).  NONNEG: T >= 0, so only non-negative bit patterns pass, with key =
+// bits + 0x8000; NaN patterns that pass are flagged, never kept.
+template <int R, bool NONNEG>
+__device__ __forceinline__ void wide_lanes_value(WaveWide<R> &w, uint4 d, uint32_t inv0, uint64_t valid,
+                                                 const Filter &f) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint64_t m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t word = dw[e >> 1];
+    const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
+    m[e] = (NONNEG ? lanes_sgt((int32_t)(int16_t)b, f.t16) : lanes_ult(b, f.tu)) & valid;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (!m[e]) continue;
+    const uint32_t word = dw[e >> 1];
+    const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
+    const uint32_t key = NONNEG ? (b > w.inf ? 0u : b | 0x8000u) : order_key(b, w.inf);
+    if (m[e] & lanes_eq(key, 0u)) w.flags |= kNan;
+    const uint32_t c = key ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
+    uint64_t h = m[e] & lanes_ugt(c, w.kth);
+    while (h) {  // against a stale k-th: extra entries land at ranks >= k only
+      const int l = __builtin_ctzll(h);
+      h &= h - 1;
+      wide_insert_one<R>(w.L, readlane(c, l));
+    }
+  }
+  w.kth = wide_at<R>(w.L, w.km1);
+}
+
+// One loaded chunk (vector u of this lane = the wave's vector first + 64 u +
+// lane): trip masks against T at the chunk start, then for each tripped
+// vector the lanes' composites above T, sorted per lane, offered position by
+// position.  Positive NaN patterns pass the value test and are flagged here.
+template <int R>
+__device__ __forceinline__ void wide_chunk(WaveWide<R> &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
+                                           int64_t col_first, int64_t base) {
+  w.ext = max(wide_bound(w.tau, w.wave), w.floor);
+  const Filter f0 = filter_for(max(w.kth >> 16, w.ext), w.flags, w.inf);
+  uint64_t vt[kChunkVecs], ft[kChunkVecs];
+  lane_trips<kChunkVecs>(v, f0, vt, ft);
+  uint64_t any_v = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint64_t valid = lanes_ult(first + (uint32_t)(u * kWave + lane_id()), nvec);
+    vt[u] &= valid;
+    ft[u] &= valid;
+    any_v |= vt[u];
+    if (ft[u]) take_flags(w.flags, w.inf, v[u], ft[u], f0.ftrip);
+  }
+  if (!any_v) return;
+  const uint32_t l = (uint32_t)lane_id();
+  // vectors rotated through x0 (no dynamic index into register arrays)
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  uint64_t m0 = vt[0], m1 = vt[1], m2 = vt[2], m3 = vt[3];
+  uint32_t iv = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
+#pragma unroll 1
+  for (int u = 0; u < kChunkVecs; ++u) {
+    if (m0 && __popcll(m0) < kWideDenseLanes) {
+      const Filter f = filter_for(max(w.kth >> 16, w.ext), w.flags, w.inf);
+      if (f.nonneg) wide_lanes_value<R, true>(w, x0, iv, m0, f);
+      else wide_lanes_value<R, false>(w, x0, iv, m0, f);
+    } else if (m0) {
+      const bool mine = (m0 >> l) & 1u;
+      const uint32_t t = max(w.kth >> 16, w.ext);
+      const uint32_t dw[4] = {x0.x, x0.y, x0.z, x0.w};
+      uint32_t c[8];
+      bool nan = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+        const uint32_t key = order_key(b, w.inf);
+        nan |= mine && key == 0;
+        c[e] = (mine && key > t) ? (key << 16) | (iv - (uint32_t)e) : 0u;
+      }
+      if (ballot(nan)) w.flags |= kNan;
+      sort8_desc(c);
+#pragma unroll 1
+      for (int p = 0; p < 8; ++p) {
+        const uint64_t m = lanes_ugt(c[0], w.kth);
+        if (!m) break;
+        wide_offer<R>(w, c[0], m);
+        c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7]; c[7] = 0;
+      }
+      // the kept set just grew a lot: share it and take the others' news
+      wide_publish<R>(w);
+      w.ext = max(wide_bound(w.tau, w.wave), w.floor);
+    }
+    m0 = m1;
+    m1 = m2;
+    m2 = m3;
+    m3 = 0;
+    if (!(m0 | m1 | m2)) break;
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+    iv -= (uint32_t)(kWave * kVecElems);
+  }
+  wide_publish<R>(w);
+}
+
+// Columns [lo, hi) one per lane (row edges, tiny spans).
+template <int R>
+__device__ void wide_columns(WaveWide<R> &w, const uint16_t *row, int64_t lo, int64_t hi, int64_t base) {
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? (uint32_t)row[col] : 0u;
+    const uint32_t key = order_key(b, w.inf);
+    if (ballot(valid && (b & 0x7FFFu) > w.inf)) w.flags |= kNan;
+    if (ballot(valid && b == (0x8000u | w.inf))) w.flags |= kNinf;
+    const uint32_t c = (valid && key > w.ext) ? (key << 16) | (0xFFFFu - (uint32_t)(col - base)) : 0u;
+    const uint64_t m = lanes_ugt(c, w.kth);
+    if (m) wide_offer<R>(w, c, m);
+  }
+}
+
+// ---- R-register lists of 64-bit composites (the fold of split rows) ----
+
+__device__ __forceinline__ uint64_t bitonic_merge64_u64(uint64_t v, const Xchg &x) {
+  v = cx_stage64<32, 32>(v, x);
+  v = cx_stage64<16, 16>(v, x);
+  v = cx_stage64<8, 8>(v, x);
+  v = cx_stage64<4, 4>(v, x);
+  v = cx_stage64<2, 2>(v, x);
+  v = cx_stage64<1, 1>(v, x);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  return ((uint64_t)readlane((uint32_t)(v >> 32), l) << 32) | readlane((uint32_t)v, l);
+}
+
+// Merges the sorted list B (R registers, descending, 0 = none) into A.
+template <int R>
+__device__ __forceinline__ void wide_merge_lists64(uint64_t (&A)[R], const uint64_t (&B)[R], const Xchg &x) {
+#pragma unroll
+  for (int jb = 0; jb < R; ++jb) {
+    uint64_t v = B[jb];
+    if (!ballot(v != 0)) break;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (!ballot(v != 0)) break;
+      if (readlane64(v, 0) <= readlane64(A[j], kWave - 1)) continue;
+      const uint64_t rv = partner64<63>(v, x);
+      const uint64_t hi = A[j] > rv ? A[j] : rv, lo = A[j] > rv ? rv : A[j];
+      A[j] = bitonic_merge64_u64(hi, x);
+      if (j + 1 < R) v = bitonic_merge64_u64(lo, x);
+    }
+  }
+}
+
+// Last-workgroup fold of a split row (the protocol of the k <= 64 scan):
+// arrival counted after the span's stores completed; the last arrival loads
+// every span list with agent-scope loads, each wave folding lists wave,
+// wave + 4, ..., then a tree over the four waves through LDS.
+template <int R>
+__device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, int S, const uint16_t *row, int wave,
+                                                  int l, uint64_t (*s_acc)[kWave * R]) {
+  __shared__ int s_last;
+  __shared__ int32_t s_cnt[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+  const int64_t rb = r - a.row0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const Xchg x = make_xchg();
+  const int k = a.k;
+  uint64_t acc[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = 0;
+  int cnt = 0;
+  uint32_t fl = 0;
+  for (int i = wave; i < S; i += kWgWaves) {
+    const int64_t sb = r * S + i;
+    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent);
+    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
+    uint64_t B[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = j * kWave + l;
+      B[j] = e < c ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+    }
+    cnt += c;
+    if (i == wave) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] = B[j];
+    } else {
+      wide_merge_lists64<R>(acc, B, x);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) s_acc[wave][j * kWave + l] = acc[j];
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_fl[wave] = fl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int step = 1; step < kWgWaves; step *= 2) {
+    if (wave % (2 * step) == 0) {
+      uint64_t B[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) B[j] = s_acc[wave + step][j * kWave + l];
+      wide_merge_lists64<R>(acc, B, x);
+#pragma unroll
+      for (int j = 0; j < R; ++j) s_acc[wave][j * kWave + l] = acc[j];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+#pragma unroll
+  for (int o = 1; o < kWgWaves; ++o) {
+    cnt += s_cnt[o];
+    fl |= s_fl[o];
+  }
+  if (cnt > k) cnt = k;
+  const int64_t ob = r * k;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int e = j * kWave + l;
+    if (e < k) {
+      if (e < cnt) {
+        a.out_idx[ob + e] = (int32_t)(col_of(acc[j]) + a.col_base);
+        a.out_val[ob + e] = value_bits(acc[j], row);
+      } else {
+        a.out_idx[ob + e] = TK_FILL_IDX;
+        a.out_val[ob + e] = (uint16_t)TK_FILL_VAL;
+      }
+    }
+  }
+  if (l == 0) {
+    a.out_count[r] = cnt;
+    a.out_nonfinite[r] = fl;
+    __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
+  __shared__ uint64_t s_list[kWgWaves][kWave * R];
+  __shared__ int32_t s_count[kWgWaves];
+  __shared__ uint32_t s_flags[kWgWaves];
+  __shared__ uint32_t s_tau[2 * kWgWaves];
+  __shared__ uint32_t s_samp[kWgWaves][kWave];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const uint16_t *row = a.in + r * a.stride;
+
+  // the span and wave shares of the k <= 64 scan
+  const int64_t a0 = (int64_t)((8u - (uint32_t)(((uintptr_t)row >> 1) & 7u)) & 7u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kVecElems : 0;
+  int64_t j0 = 0, j1 = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kVecElems * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+  const int64_t base = (wave == 0 && head_hi > 0) ? 0 : a0 + kVecElems * wv0;
+  const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t wn = (uint32_t)(wv1 - wv0);
+
+  // Floors from the workgroup's 256 first-chunk lane maxima, as in the k <= 64
+  // scan: exact = the k-th largest (k lanes hold an element at or above it);
+  // speculative = the spec_rank-th largest (spec_rank < k, chosen on the host
+  // from k and the span width), verified after the scan -- if the lists then
+  // hold k entries, everything dropped is beaten by k kept ones; otherwise the
+  // span is scanned again under the exact floor.
+  const Xchg x = make_xchg();
+  uint4 A[kChunkVecs];
+  if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
+  s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn, a.inf) : 0u, x);
+  __syncthreads();
+  uint32_t exact_floor, spec_floor = 0;
+  {
+    uint32_t P[R];
+    P[0] = s_samp[0][l];
+#pragma unroll
+    for (int j = 1; j < R; ++j) P[j] = 0;
+#pragma unroll
+    for (int o = 1; o < kWgWaves; ++o) wide_merge_batch<R>(P, s_samp[o][l], x);
+    const uint32_t te = wide_at<R>(P, a.k - 1);
+    exact_floor = te > 0 ? te - 1 : 0;
+    if (a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks * kChunkVecs * kWave) {
+      const uint32_t ts = wide_at<R>(P, a.spec_rank - 1);
+      spec_floor = ts > 0 ? ts - 1 : 0;
+    }
+  }
+  uint32_t floor = exact_floor;
+  bool verify = false;
+  if (spec_floor > exact_floor) {
+    floor = spec_floor;
+    verify = true;
+  }
+
+  WaveWide<R> w;
+  int total = 0;
+  uint32_t flags = 0;
+  for (;;) {
+    if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
+    __syncthreads();
+    w.x = x;
+#pragma unroll
+    for (int j = 0; j < R; ++j) w.L[j] = 0;
+    w.kth = 0;
+    w.ext = floor;
+    w.floor = floor;
+    w.flags = 0;
+    w.inf = a.inf;
+    w.km1 = a.k - 1;
+    w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
+    w.wave = wave;
+    w.tau = s_tau;
+
+    if (wave == 0 && head_hi > 0) wide_columns<R>(w, row, 0, head_hi, base);
+    if (wn > 0) {
+      constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+      const uint32_t lane_off = (uint32_t)l * 16u;
+      const int64_t col_first = a0 + kVecElems * wv0;
+      uint4 B[kChunkVecs];
+      for (uint32_t first = 0; first < wn; first += 2 * kStep) {
+        load_chunk(B, wvp, wn, first + kStep, lane_off);
+        wide_chunk<R>(w, A, first, wn, col_first, base);
+        if (first + kStep >= wn) break;
+        load_chunk(A, wvp, wn, first + 2 * kStep, lane_off);
+        wide_chunk<R>(w, B, first + kStep, wn, col_first, base);
+      }
+    }
+    if (wave == kWgWaves - 1 && tail_hi > tail_lo) wide_columns<R>(w, row, tail_lo, tail_hi, base);
+
+    // the wave's list, its count and flags to LDS
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      s_list[wave][j * kWave + l] = composite64(w.L[j], base);
+      cnt += __popcll(ballot(w.L[j] != 0));
+    }
+    if (l == 0) {
+      s_count[wave] = cnt < a.k ? cnt : a.k;
+      s_flags[wave] = w.flags | ((readlane(w.L[0], 0) >> 16) == 0x8000u + a.inf ? kPinf : 0u);
+    }
+    __syncthreads();
+    total = 0;
+    flags = 0;
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o) {
+      total += s_count[o];
+      flags |= s_flags[o];
+    }
+    if (!verify || total >= a.k) break;  // exact, or the speculation verified
+    floor = exact_floor;
+    verify = false;
+    if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
+    __syncthreads();  // every wave has read the counts above
+  }
+  if (total > a.k) total = a.k;
+
+  // rank of each kept entry in the union of the four lists
+  const int64_t sb = r * S + s;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int e = j * kWave + l;
+    if (e >= s_count[wave]) continue;
+    const uint64_t xv = s_list[wave][e];
+    int rank = e;
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o)
+      if (o != wave) rank += count_beating(s_list[o], s_count[o], xv);
+    if (rank >= a.k) continue;
+    if (S == 1) {
+      a.out_idx[r * a.k + rank] = (int32_t)(col_of(xv) + a.col_base);
+      a.out_val[r * a.k + rank] = value_bits(xv, row);
+    } else {
+      __hip_atomic_store(&a.span_list[sb * a.k + rank], xv, __ATOMIC_RELAXED, kAgent);
+    }
+  }
+  if (S == 1) {
+    const int t = threadIdx.x;
+    if (t >= total && t < a.k) {
+      a.out_idx[r * a.k + t] = TK_FILL_IDX;
+      a.out_val[r * a.k + t] = (uint16_t)TK_FILL_VAL;
+    }
+    if (t == 0) {
+      a.out_count[r] = total;
+      a.out_nonfinite[r] = flags;
+    }
+    return;
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
+    __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
+  }
+  // the rank merge's reads of s_list are done once every wave has passed this
+  // point; the fold then reuses s_list as its exchange buffer
+  __syncthreads();
+  wide_fold_if_last<R>(a, r, S, row, wave, l, s_list);
+}
+
+}  // namespace
+
+hipError_t launch_wide_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream) {
+  if (rows_in_launch <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)(rows_in_launch * a.spans)), block(kWgThreads);
+  if (a.k <= 2 * kWave) {
+    hipLaunchKernelGGL(wide_scan_kernel<2>, grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(wide_scan_kernel<4>, grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tk
