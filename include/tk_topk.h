@@ -259,6 +259,45 @@ tk_status tk_validate_sample_bf16(int64_t rows, int32_t k, const int32_t *idx, c
                                   const int32_t *count, float temperature, float top_p, const int32_t *out_token,
                                   const int32_t *out_kept);
 
+/*
+ * Draft-head logits fused with the row top-k.  The drafter of TensorFold PR
+ * #713 computes its draft head and takes the top k of each of its rows (15
+ * rows of 98592 columns in change 3); this call does both in one pass over
+ * the head's weights, so the logits are never written to memory.  The pages
+ * give no kernel for the head; the library's reading:
+ *   logits[r][n] = bf16_rne( sum_i h[r][i] * w[n][i] )
+ * with the products and their sum in float32 on the matrix cores (the
+ * summation order is the hardware's; the result is within float32
+ * accumulation error of the exact sum before the bf16 rounding to nearest,
+ * ties to even; NaN inputs give NaN logits), and then exactly the top-k of
+ * tk_topk_bf16 over those logits (order, NaN, infinities, flags, fills).
+ *   h      bf16 [rows][h_stride], 16-byte aligned, h_stride % 8 == 0
+ *   w      bf16 [vocab][w_stride] (vocabulary-major, as a linear layer's
+ *          weight), 16-byte aligned, w_stride % 8 == 0
+ *   out_*  as tk_topk_bf16 ([rows][k] entries with vocabulary indices,
+ *          [rows] counts and masks)
+ *   logits NULL, or bf16 [rows][logits_stride] (logits_stride >= vocab,
+ *          2-byte aligned) that also receives the logits -- for tests; the
+ *          top-k does not depend on it.
+ * Guards: 0 <= rows <= TK_HEAD_MAX_ROWS, 32 <= hidden <= 65536 with hidden %
+ * 32 == 0, 1 <= vocab <= INT32_MAX, hidden <= h_stride, w_stride <= 2^21
+ * (TK_ERR_SHAPE); 1 <= k <= TK_MAX_K_LANE (TK_ERR_K); NULL (logits may be
+ * NULL), alignment, and outputs overlapping each other or an input
+ * (TK_ERR_ALIAS).  Asynchronous on `stream`; scratch as tk_topk_bf16.
+ */
+#define TK_HEAD_MAX_ROWS 64
+
+tk_status tk_head_topk_bf16(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h,
+                            int64_t h_stride, const uint16_t *w, int64_t w_stride, int32_t *out_idx,
+                            uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, uint16_t *logits,
+                            int64_t logits_stride, void *stream);
+
+/* The host-side guards of tk_head_topk_bf16 alone (no HIP call). */
+tk_status tk_validate_head_bf16(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h,
+                                int64_t h_stride, const uint16_t *w, int64_t w_stride, const int32_t *out_idx,
+                                const uint16_t *out_val, const int32_t *out_count, const uint32_t *out_nonfinite,
+                                const uint16_t *logits, int64_t logits_stride);
+
 int32_t tk_max_k(void);             /* == TK_MAX_K */
 int64_t tk_max_span_cols(void);     /* widest span one workgroup scans */
 const char *tk_status_string(tk_status s);

@@ -15,6 +15,7 @@ from .gen import (  # noqa: F401
     bf16_to_f16_bits,
     bf16_to_f32_bits,
     family_rows,
+    head_inputs,
     make_config_input,
     poison_padding,
     sha256_of,

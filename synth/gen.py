@@ -398,3 +398,30 @@ def family_rows(name: str, rows: int, cols: int, stride: int | None = None, seed
     if fmt == "f16" and stride > cols:
         m[:, cols:] = bf16_to_f16_bits(m[:, cols:])  # poison stays poison: +inf and NaN patterns
     return m
+
+
+def head_inputs(rows: int, hidden: int, vocab: int, seed: int = 0, h_pad: int = 0, w_pad: int = 0,
+                kind: str = "normal"):
+    """Draft-head inputs as bf16 bit patterns: hidden states h [rows][hidden
+    + h_pad] ~ N(0, 1) and a vocabulary-major weight w [vocab][hidden + w_pad]
+    ~ N(0, 1 / sqrt(hidden)), so that logits are of unit scale; padding is
+    NaN poison.  kinds: "normal"; "ties" (w rows repeated in blocks of 4, so
+    equal logits occur); "integers" (small integers in h and w: exact sums);
+    "nonfinite" (a few +-inf and NaN in h)."""
+    rng = np.random.default_rng(0x4EAD0000 + seed)
+    h = rng.standard_normal((rows, hidden)).astype(np.float32)
+    w = (rng.standard_normal((vocab, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    if kind == "ties":
+        w = np.repeat(w[: (vocab + 3) // 4], 4, axis=0)[:vocab]
+    elif kind == "integers":
+        h = rng.integers(-4, 5, size=(rows, hidden)).astype(np.float32)
+        w = rng.integers(-4, 5, size=(vocab, hidden)).astype(np.float32)
+    elif kind == "nonfinite" and rows > 0:
+        for r in range(0, rows, 3):
+            h[r, rng.integers(0, hidden)] = [np.inf, -np.inf, np.nan][r % 3]
+    hb = np.full((rows, hidden + h_pad), 0x7FC0, dtype=np.uint16)
+    wb = np.full((vocab, hidden + w_pad), 0x7FC0, dtype=np.uint16)
+    hb[:, :hidden] = f32_to_bf16_bits(h)
+    wb[:, :hidden] = f32_to_bf16_bits(w)
+    return hb, wb
+

@@ -250,3 +250,29 @@ def test_f32_guards():
     import ctypes
 
     assert lib.tk_topk_f32_ex(0, 100, 100, 8, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(opt)) == OPTION
+
+
+W_FAKE = 0x100000000  # above every other fake address: the weights span 404 MB
+
+
+def vh(rows=15, hidden=2048, vocab=98592, k=32, h=0x1000000, hs=2048, w=W_FAKE, ws=2048, idx=IDX, val=VAL,
+       cnt=CNT, msk=MSK, lg=None, ls=0):
+    return tk.validate_head(rows, hidden, vocab, k, h, hs, w, ws, idx, val, cnt, msk, lg, ls)
+
+
+def test_head_guards():
+    assert vh() == OK and vh(rows=64) == OK and vh(rows=1, vocab=1, hidden=32, hs=32, ws=32) == OK
+    assert vh(rows=0, h=None, w=None, idx=None, val=None, cnt=None, msk=None) == OK
+    assert vh(rows=65) == SHAPE and vh(rows=-1) == SHAPE
+    assert vh(hidden=16, hs=16, ws=16) == SHAPE and vh(hidden=48, hs=48, ws=48) == SHAPE  # multiple of 32
+    assert vh(hidden=65536 + 32, hs=65568, ws=65568) == SHAPE and vh(vocab=0) == SHAPE
+    assert vh(hs=2047) == SHAPE and vh(ws=2052) == SHAPE and vh(ws=2**21 + 8) == SHAPE    # strides
+    assert vh(k=0) == K and vh(k=65) == K and vh(k=64) == OK
+    assert vh(h=None) == NULL and vh(msk=None) == NULL
+    assert vh(h=0x1000008) == ALIGN and vh(w=W_FAKE + 2) == ALIGN and vh(val=VAL + 1) == ALIGN
+    assert vh(lg=0x60000000, ls=98592) == OK and vh(lg=0x60000000, ls=98591) == SHAPE
+    assert vh(lg=0x60000001, ls=98592) == ALIGN
+    assert vh(idx=W_FAKE + 1024) == ALIAS                  # an output inside the weights
+    assert vh(lg=VAL - 64, ls=98592) == ALIAS               # logits over an output
+    assert vh(cnt=MSK) == ALIAS
+

@@ -35,7 +35,8 @@ FILL_IDX, FILL_VAL = -1, 0x7FC0
 EXPORTS = (
     "tk_topk_bf16", "tk_topk_bf16_ex", "tk_topk_f16", "tk_topk_f16_ex", "tk_topk_f32", "tk_topk_f32_ex",
     "tk_validate_f32", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
-    "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
+    "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_head_topk_bf16",
+    "tk_validate_head_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
 )
 
 
@@ -100,6 +101,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_sample_topk_bf16.argtypes = [i64, i32, vp, vp, vp, f32, f32, u64, u64, vp, vp, vp]
     lib.tk_validate_sample_bf16.restype = i32
     lib.tk_validate_sample_bf16.argtypes = [i64, i32, vp, vp, vp, f32, f32, vp, vp]
+    lib.tk_head_topk_bf16.restype = i32
+    lib.tk_head_topk_bf16.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, i64, vp]
+    lib.tk_validate_head_bf16.restype = i32
+    lib.tk_validate_head_bf16.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, vp, vp, vp, vp, i64]
     lib.tk_plan_spans.restype = i32
     lib.tk_plan_spans.argtypes = [i64, i64, i32, i32]
     lib.tk_max_k.restype = i32
@@ -301,6 +306,50 @@ def sample_topk_bf16(topk: TopK, temperature: float, top_p: float, seed: int, of
     if status != TK_OK:
         raise TkError(status, "tk_sample_topk_bf16")
     return out
+
+
+def head_topk_bf16(h, w, k: int, *, logits: bool = False, out: TopK | None = None):
+    """Draft-head logits h . w^T fused with the row top-k (tk_head_topk_bf16).
+
+    ``h``: bf16 [rows][hidden] (rows <= 64), ``w``: bf16 [vocab][hidden], both
+    with contiguous last dimensions and row strides that are multiples of 8
+    elements, 16-byte aligned.  Returns the TopK of the bf16 logits; with
+    ``logits=True`` returns (TopK, logits [rows][vocab] bf16) -- the logits are
+    otherwise never materialised.
+    """
+    import torch
+
+    if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+        raise ValueError("expected h [rows][hidden] and w [vocab][hidden]")
+    for t in (h, w):
+        if t.dtype not in (torch.bfloat16, torch.int16) or t.device.type != "cuda":
+            raise TypeError("expected bf16 tensors on a HIP device")
+        if t.shape[0] > 0 and t.stride(1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    rows, hidden = h.shape
+    vocab = w.shape[0]
+    if out is None:
+        out = TopK(torch.empty((rows, k), dtype=torch.int32, device=h.device),
+                   torch.empty((rows, k), dtype=torch.bfloat16, device=h.device),
+                   torch.empty((rows,), dtype=torch.int32, device=h.device),
+                   torch.empty((rows,), dtype=torch.int32, device=h.device))
+    lg = torch.empty((rows, vocab), dtype=torch.bfloat16, device=h.device) if logits else None
+    dev = h.device.index if h.device.index is not None else torch.cuda.current_device()
+    status = int(load().tk_head_topk_bf16(
+        rows, hidden, vocab, k, h.data_ptr(), h.stride(0) if rows > 1 else hidden, w.data_ptr(),
+        w.stride(0) if vocab > 1 else hidden, out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
+        out.nonfinite.data_ptr(), lg.data_ptr() if lg is not None else None, vocab if lg is not None else 0,
+        _current_stream_handle(torch, dev)))
+    if status != TK_OK:
+        raise TkError(status, "tk_head_topk_bf16")
+    return (out, lg) if logits else out
+
+
+def validate_head(rows, hidden, vocab, k, h_ptr, h_stride, w_ptr, w_stride, idx_ptr, val_ptr, count_ptr, mask_ptr,
+                  logits_ptr=None, logits_stride=0) -> int:
+    """The host-side guards of tk_head_topk_bf16 on raw pointers (no HIP call)."""
+    return int(load().tk_validate_head_bf16(rows, hidden, vocab, k, h_ptr, h_stride, w_ptr, w_stride, idx_ptr,
+                                            val_ptr, count_ptr, mask_ptr, logits_ptr, logits_stride))
 
 
 def validate_sample(rows, k, idx_ptr, val_ptr, count_ptr, temperature, top_p, token_ptr, kept_ptr) -> int:

@@ -16,7 +16,8 @@ ARCH = os.environ.get("TK_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "tk_kernels.hip"), os.path.join(CSRC, "tk_sample.hip"), os.path.join(CSRC, "tk_f32.hip"),
-           os.path.join(CSRC, "tk_wide.hip"), os.path.join(CSRC, "tk_api.cpp")]
+           os.path.join(CSRC, "tk_wide.hip"), os.path.join(CSRC, "tk_head.hip"),
+           os.path.join(CSRC, "tk_api.cpp")]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

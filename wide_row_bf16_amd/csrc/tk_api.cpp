@@ -106,6 +106,43 @@ tk_status guard_merge(int64_t rows, int32_t shards, int32_t k, const void *idx_i
   return TK_OK;
 }
 
+// Guards of the fused head: shapes, strides and limits that keep every
+// buffer offset of a workgroup within 32 bits, alignment of the 16-byte
+// fragment loads, and no output overlapping another or an input.
+constexpr int64_t kHeadMaxHidden = 65536;
+constexpr int64_t kHeadMaxStride = int64_t(1) << 21;
+
+tk_status guard_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const void *h, int64_t h_stride,
+                     const void *w, int64_t w_stride, const void *out_idx, const void *out_val, const void *out_count,
+                     const void *out_nonfinite, const void *logits, int64_t logits_stride) {
+  if (rows < 0 || rows > TK_HEAD_MAX_ROWS) return TK_ERR_SHAPE;
+  if (hidden < 32 || hidden > kHeadMaxHidden || hidden % 32 != 0) return TK_ERR_SHAPE;
+  if (vocab < 1 || vocab > INT32_MAX) return TK_ERR_SHAPE;
+  if (h_stride < hidden || w_stride < hidden || h_stride % 8 != 0 || w_stride % 8 != 0) return TK_ERR_SHAPE;
+  if (h_stride > kHeadMaxStride || w_stride > kHeadMaxStride) return TK_ERR_SHAPE;
+  if (logits && logits_stride < vocab) return TK_ERR_SHAPE;
+  if (k < 1 || k > kMaxK) return TK_ERR_K;
+  if (rows == 0) return TK_OK;
+  if (!h || !w || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;
+  if (((uintptr_t)h & 15) || ((uintptr_t)w & 15)) return TK_ERR_ALIGN;
+  if (((uintptr_t)out_val & 1) || ((uintptr_t)logits & 1)) return TK_ERR_ALIGN;
+  if (((uintptr_t)out_idx & 3) || ((uintptr_t)out_count & 3) || ((uintptr_t)out_nonfinite & 3)) return TK_ERR_ALIGN;
+  const Range rs[7] = {
+      {(uintptr_t)h, (uintptr_t)h + (uintptr_t)(2 * ((rows - 1) * h_stride + hidden))},
+      {(uintptr_t)w, (uintptr_t)w + (uintptr_t)(2 * ((vocab - 1) * w_stride + hidden))},
+      {(uintptr_t)out_idx, (uintptr_t)out_idx + (uintptr_t)(4 * rows * k)},
+      {(uintptr_t)out_val, (uintptr_t)out_val + (uintptr_t)(2 * rows * k)},
+      {(uintptr_t)out_count, (uintptr_t)out_count + (uintptr_t)(4 * rows)},
+      {(uintptr_t)out_nonfinite, (uintptr_t)out_nonfinite + (uintptr_t)(4 * rows)},
+      {(uintptr_t)logits, logits ? (uintptr_t)logits + (uintptr_t)(2 * ((rows - 1) * logits_stride + vocab))
+                                 : (uintptr_t)logits},
+  };
+  for (int i = 2; i < 7; ++i)
+    for (int j = 0; j < 7; ++j)
+      if (j != i && overlap(rs[i], rs[j])) return TK_ERR_ALIAS;
+  return TK_OK;
+}
+
 // Guards of the sampling call: inputs [rows][k] entries and [rows] counts.
 tk_status guard_sample(int64_t rows, int32_t k, const void *idx, const void *val, const void *count, float temperature,
                        float top_p, const void *out_token, const void *out_kept) {
@@ -442,6 +479,90 @@ tk_status run_wide(int64_t rows, int64_t cols, int64_t stride, int32_t k, const 
     }
   }
   if (owned && hipFreeAsync(base, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  return result;
+}
+
+// Fused head: the head kernel writes one candidate list per (row, span of
+// kHeadSpanCols columns); span_merge_kernel levels (groups of up to
+// kMergeGroup lists, at least one level) fold them into the outputs.
+tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h, int64_t h_stride,
+                   const uint16_t *w, int64_t w_stride, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
+                   uint32_t *out_nonfinite, uint16_t *logits, int64_t logits_stride, hipStream_t stream, int dev) {
+  const int64_t spans = (vocab + tk::kHeadSpanCols - 1) / tk::kHeadSpanCols;
+  // merge levels: lists in per row at each level; the last level has one
+  // group per row (lists_out == 1) and writes the outputs, every earlier level
+  // writes the next level's lists (span_merge_kernel tells the two apart by
+  // lists_out alone)
+  int64_t level_lists[8];
+  int levels = 0;
+  int64_t n = spans;
+  do {
+    level_lists[levels++] = n;
+    n = (n + kMergeGroup - 1) / kMergeGroup;
+  } while (n > 1);
+  size_t off_list[8], off_count[8], off_flags[8], total = 0;
+  for (int i = 0; i < levels; ++i) {
+    const size_t nlists = (size_t)rows * (size_t)level_lists[i];
+    off_list[i] = total;
+    total = align256(total + nlists * (size_t)k * sizeof(uint64_t));
+    off_count[i] = total;
+    total = align256(total + nlists * sizeof(int32_t));
+    off_flags[i] = total;
+    total = align256(total + nlists * sizeof(uint32_t));
+  }
+  const size_t off0 = align256((size_t)kFusedMaxRows * sizeof(int32_t));  // the counters stay untouched
+  keep_pool(dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  char *base = nullptr;
+  bool owned = false;
+  const tk_status sst = acquire_scratch(dev, stream, off0 + total, &base, &owned);
+  if (sst != TK_OK) return sst;
+  base += off0;
+  tk_status result = TK_OK;
+  tk::HeadArgs ha{};
+  ha.rows = rows;
+  ha.hidden = hidden;
+  ha.vocab = vocab;
+  ha.k = k;
+  ha.spans = (int32_t)spans;
+  ha.h = h;
+  ha.h_stride = h_stride;
+  ha.w = w;
+  ha.w_stride = w_stride;
+  ha.span_list = (uint64_t *)(base + off_list[0]);
+  ha.span_count = (int32_t *)(base + off_count[0]);
+  ha.span_flags = (uint32_t *)(base + off_flags[0]);
+  ha.logits = logits;
+  ha.logits_stride = logits_stride;
+  if (tk::launch_head_scan(ha, stream) != hipSuccess) result = TK_ERR_DEVICE;
+  for (int i = 0; i < levels && result == TK_OK; ++i) {
+    tk::MergeArgs m{};
+    m.in = nullptr;
+    m.row0 = 0;
+    m.k = k;
+    m.lists_in = (int32_t)level_lists[i];
+    m.group = m.lists_in < kMergeGroup ? m.lists_in : kMergeGroup;
+    m.lists_out = (m.lists_in + m.group - 1) / m.group;
+    m.list_in = (const uint64_t *)(base + off_list[i]);
+    m.count_in = (const int32_t *)(base + off_count[i]);
+    m.flags_in = (const uint32_t *)(base + off_flags[i]);
+    if ((m.lists_out == 1) != (i + 1 == levels)) {  // the level plan and the kernel's test must agree
+      result = TK_ERR_DEVICE;
+      break;
+    }
+    if (i + 1 < levels) {
+      m.list_out = (uint64_t *)(base + off_list[i + 1]);
+      m.count_out = (int32_t *)(base + off_count[i + 1]);
+      m.flags_out = (uint32_t *)(base + off_flags[i + 1]);
+    } else {
+      m.out_idx = out_idx;
+      m.out_val = out_val;
+      m.out_count = out_count;
+      m.out_nonfinite = out_nonfinite;
+    }
+    if (tk::launch_span_merge(m, rows, stream) != hipSuccess) result = TK_ERR_DEVICE;
+  }
+  if (owned && hipFreeAsync(base - off0, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
   return result;
 }
 
@@ -810,6 +931,27 @@ tk_status tk_sample_topk_bf16(int64_t rows, int32_t k, const int32_t *idx, const
   a.out_token = out_token;
   a.out_kept = out_kept;
   return tk::launch_sample(a, (hipStream_t)stream) == hipSuccess ? TK_OK : TK_ERR_DEVICE;
+}
+
+tk_status tk_validate_head_bf16(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h,
+                                int64_t h_stride, const uint16_t *w, int64_t w_stride, const int32_t *out_idx,
+                                const uint16_t *out_val, const int32_t *out_count, const uint32_t *out_nonfinite,
+                                const uint16_t *logits, int64_t logits_stride) {
+  return guard_head(rows, hidden, vocab, k, h, h_stride, w, w_stride, out_idx, out_val, out_count, out_nonfinite,
+                    logits, logits_stride);
+}
+
+tk_status tk_head_topk_bf16(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h,
+                            int64_t h_stride, const uint16_t *w, int64_t w_stride, int32_t *out_idx,
+                            uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, uint16_t *logits,
+                            int64_t logits_stride, void *stream) {
+  const tk_status st = guard_head(rows, hidden, vocab, k, h, h_stride, w, w_stride, out_idx, out_val, out_count,
+                                  out_nonfinite, logits, logits_stride);
+  if (st != TK_OK || rows == 0) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  return run_head(rows, hidden, vocab, k, h, h_stride, w, w_stride, out_idx, out_val, out_count, out_nonfinite,
+                  logits, logits_stride, (hipStream_t)stream, dev);
 }
 
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {

@@ -27,11 +27,14 @@ constexpr int kBatchInsert = 8;                // >= this many new candidates: b
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
 constexpr int kSampleElems = kWgWaves * kChunkVecs * kWave * kVecElems;  // pooled sample: each wave's first chunk
 constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
+constexpr int kHeadSpanCols = 256;             // vocabulary columns per workgroup of the fused head
+constexpr int kHeadMaxRows = 64;               // rows of the fused head: four 16-row matrix-core tiles
 
 static_assert(kMaxKWide == (int)TK_MAX_K, "public and internal max k differ");
 static_assert(kMaxK == (int)TK_MAX_K_LANE, "public and internal lane max k differ");
 static_assert(kMaxKWide == 4 * kWave, "the multi-register scan keeps at most four registers");
 static_assert(kMaxK <= kWave, "a wave holds one kept entry per lane");
+static_assert(kHeadMaxRows == (int)TK_HEAD_MAX_ROWS, "public and internal head row limits differ");
 static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
 // A wave scans at most ceil(kMaxSpanVecs / kWgWaves) vectors plus two partial
 // edges of < kVecElems columns each; its columns must stay within 16 bits.

@@ -1,0 +1,232 @@
+// Draft-head logits fused with the row top-k (gfx950): logits = h . w^T for
+// up to 64 rows of hidden states h [rows][hidden] against a vocabulary-major
+// weight w [vocab][hidden] (bf16, fp32 accumulation, rounded to bf16), and the
+// k best logits of every row in the library's order -- without the logits
+// ever being written to memory.
+//
+// What is computed: the drafter of TensorFold PR #713 runs its draft head and
+// then the top-k over its rows (15 rows of 98592 columns in change 3); the
+// pages give no kernel for the head.  This is the plain reading: each logit
+// is the bf16 rounding (to nearest, ties to even) of the fp32 sum of the
+// products h[r][i] * w[n][i]; the top-k then follows the rules of
+// tk_topk_bf16 on those logits (score descending, lower column first, NaN
+// excluded and flagged, infinities ranked and flagged).
+//
+// Kernel.  One workgroup per span of kHeadSpanCols vocabulary columns, four
+// waves, each owning four 16-column tiles.  The contraction runs on the
+// matrix cores: v_mfma_f32_16x16x32_bf16 with A = a 16-row tile of h and B =
+// 32 hidden values of 16 vocabulary rows of w (each lane loads 16 contiguous
+// bytes of one w row: lane l takes row l % 16, values 8 (l / 16) .. + 7), one
+// accumulator per (column tile, row tile); the loads of the next hidden steps
+// are in flight while the current ones multiply.  w is read once; h is small
+// and shared by every workgroup.  Buffer
+// descriptors clamp both: rows past vocab or past rows read zero.  The
+// accumulators are rounded to bf16 into LDS; then each wave takes rows w,
+// w + 4, ... and keeps the span's top k of the row in one VGPR (lane i = i-th
+// best), as the scan kernels do, and writes it as 64-bit composites
+// key << 32 | (0x7FFFFFFF - column) << 1 | sign (the sign tells -0 from +0,
+// which share a key) for span_merge_kernel to fold.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tk_config.h"
+#include "tk_launch.h"
+
+namespace tk {
+namespace {
+
+#include "tk_wave.h"
+#include "tk_scan16.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kWgWaves;
+constexpr int kHeadUnroll = 2;  // hidden steps of 32 per register group (two groups in flight)
+static_assert(kHeadTilesPerWave == 4, "each wave owns four 16-column tiles");
+static_assert(kHeadSpanCols <= 8 * kWave, "a row's span fits eight columns per lane");
+
+template <int POLICY>
+__device__ __forceinline__ bf16x8 load_frag(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, POLICY);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp32 -> bf16 bits, rounding to nearest with ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Fragments of kHeadUnroll hidden steps: B of this wave's four column tiles
+// (w) and A of each 16-row tile (h).
+template <int RT>
+struct HeadFrags {
+  bf16x8 b[kHeadUnroll][kHeadTilesPerWave];
+  bf16x8 a[kHeadUnroll][RT];
+};
+
+// An offset past every descriptor's range (ranges stay below 2^30 bytes and
+// the per-lane offsets below 2^30 too, so the sum cannot wrap): such a load
+// returns zeros.
+constexpr uint32_t kHeadPastEnd = 0x7FFFFFF0u;
+
+// Loads hidden steps [s0, s0 + kHeadUnroll); steps at or past `steps` read
+// zeros through an out-of-range offset instead of a branch, so that the
+// compiler keeps the other group's loads in flight (a conditional load makes
+// it wait for every outstanding load at the join).  w is read with the
+// default cache policy: a 128-byte line of a w row is split between two
+// consecutive steps, and nontemporal loads measured ~10% slower here.
+template <int RT>
+__device__ __forceinline__ void head_load(HeadFrags<RT> &F, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
+                                          uint32_t b_off, uint32_t b_tile, uint32_t a_off, uint32_t a_tile, int s0,
+                                          int steps) {
+#pragma unroll
+  for (int u = 0; u < kHeadUnroll; ++u) {
+    const bool in = s0 + u < steps;
+    const uint32_t koff = (uint32_t)(s0 + u) * 64u;
+#pragma unroll
+    for (int j = 0; j < kHeadTilesPerWave; ++j)
+      F.b[u][j] = load_frag<0>(rw, in ? b_off + j * b_tile + koff : kHeadPastEnd);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) F.a[u][t] = load_frag<0>(rh, in ? a_off + t * a_tile + koff : kHeadPastEnd);
+  }
+}
+
+// Steps past the end hold zeros and add nothing.
+template <int RT>
+__device__ __forceinline__ void head_mma(f32x4 (&acc)[kHeadTilesPerWave][RT], const HeadFrags<RT> &F) {
+#pragma unroll
+  for (int u = 0; u < kHeadUnroll; ++u)
+#pragma unroll
+    for (int j = 0; j < kHeadTilesPerWave; ++j)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F.a[u][t], F.b[u][j], acc[j][t], 0, 0, 0);
+}
+
+template <int RT>
+__global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
+  __shared__ uint16_t s_logit[RT * 16][kHeadSpanCols];
+
+  const int s = blockIdx.x;
+  const int64_t n0 = (int64_t)s * kHeadSpanCols;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const int64_t nvalid = a.vocab - n0 < kHeadSpanCols ? a.vocab - n0 : kHeadSpanCols;
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.w + n0 * a.w_stride), (short)0, (int)(nvalid * a.w_stride * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rh =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.h, (short)0, (int)(a.rows * a.h_stride * 2), kBufferWord3);
+
+  f32x4 acc[kHeadTilesPerWave][RT];
+#pragma unroll
+  for (int j = 0; j < kHeadTilesPerWave; ++j)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int tile0 = wave * kHeadTilesPerWave;
+  const uint32_t b_off = (uint32_t)(((int64_t)(tile0 * 16 + l % 16) * a.w_stride + 8 * (l / 16)) * 2);
+  const uint32_t b_tile = (uint32_t)(16 * a.w_stride * 2);
+  const uint32_t a_off = (uint32_t)(((int64_t)(l % 16) * a.h_stride + 8 * (l / 16)) * 2);
+  const uint32_t a_tile = (uint32_t)(16 * a.h_stride * 2);
+  const int steps = (int)(a.hidden / 32);
+
+  // Two register groups of kHeadUnroll hidden steps each: the loads of one
+  // group are in flight while the other's matrix-core work runs.
+  HeadFrags<RT> F0, F1;
+  head_load<RT>(F0, rw, rh, b_off, b_tile, a_off, a_tile, 0, steps);
+  for (int s0 = 0; s0 < steps; s0 += 2 * kHeadUnroll) {
+    head_load<RT>(F1, rw, rh, b_off, b_tile, a_off, a_tile, s0 + kHeadUnroll, steps);
+    head_mma<RT>(acc, F0);
+    if (s0 + kHeadUnroll >= steps) break;
+    head_load<RT>(F0, rw, rh, b_off, b_tile, a_off, a_tile, s0 + 2 * kHeadUnroll, steps);
+    head_mma<RT>(acc, F1);
+  }
+
+  // accumulators -> bf16 logits in LDS (and, on request, to memory)
+#pragma unroll
+  for (int j = 0; j < kHeadTilesPerWave; ++j) {
+    const int col = (tile0 + j) * 16 + l % 16;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = t * 16 + 4 * (l / 16) + i;
+        const uint32_t b = bf16_rne(acc[j][t][i]);
+        s_logit[row][col] = (uint16_t)b;
+        if (a.logits && row < a.rows && col < nvalid) a.logits[row * a.logits_stride + n0 + col] = (uint16_t)b;
+      }
+  }
+  __syncthreads();
+
+  // per row: the span's top k (8 columns per lane, as one vector of the scans)
+  const Xchg x = make_xchg();
+  const int k = a.k;
+  for (int row = wave; row < a.rows; row += kWgWaves) {
+    uint32_t c[8];
+    bool nan = false, ninf = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 8 * l + e;
+      const bool valid = col < nvalid;
+      const uint32_t b = valid ? (uint32_t)s_logit[row][col] : 0u;
+      const uint32_t key = order_key(b);
+      nan |= valid && key == 0;
+      ninf |= valid && b == 0xFF80u;
+      c[e] = (valid && key) ? (key << 16) | (0xFFFFu - (uint32_t)col) : 0u;
+    }
+    uint32_t flags = (ballot(nan) ? kNan : 0u) | (ballot(ninf) ? kNinf : 0u);
+    sort8_desc(c);
+    uint32_t list = 0, kth = 0;
+#pragma unroll 1
+    for (int p = 0; p < 8; ++p) {
+      uint64_t m = lanes_ugt(c[0], kth);
+      if (!m) break;
+      if (__popcll(m) >= kBatchInsert) {
+        list = merge_batch(list, c[0] > kth ? c[0] : 0u, x);
+      } else {
+        do {
+          const int ln = __builtin_ctzll(m);
+          m &= m - 1;
+          list = insert_one(list, readlane(c[0], ln));
+        } while (m);
+      }
+      kth = readlane(list, k - 1);
+      c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7]; c[7] = 0;
+    }
+    const int cnt = min(__popcll(ballot(list != 0)), k);
+    if ((readlane(list, 0) >> 16) == 0xFF80u) flags |= kPinf;
+    const int64_t sb = (int64_t)row * a.spans + s;
+    if (l < cnt) {
+      const uint32_t key = list >> 16;
+      const uint32_t col = 0xFFFFu - (list & 0xFFFFu);
+      const uint32_t sign = key == 0x8000u ? (uint32_t)(s_logit[row][col] >> 15) : 0u;
+      a.span_list[sb * k + l] =
+          ((uint64_t)key << 32) | ((uint64_t)(0x7FFFFFFFu - (uint32_t)(n0 + col)) << 1) | sign;
+    }
+    if (l == 0) {
+      a.span_count[sb] = cnt;
+      a.span_flags[sb] = flags;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_head_scan(const HeadArgs &a, hipStream_t stream) {
+  if (a.rows <= 0 || a.spans <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)a.spans), block(kWgThreads);
+  if (a.rows <= 16) {
+    hipLaunchKernelGGL(head_scan_kernel<1>, grid, block, 0, stream, a);
+  } else if (a.rows <= 32) {
+    hipLaunchKernelGGL(head_scan_kernel<2>, grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(head_scan_kernel<4>, grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tk

@@ -818,12 +818,14 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
   const uint32_t flags = s_flags;
 
   if (a.lists_out == 1) {
-    const uint16_t *row = a.in + r * a.stride;
     const int64_t ob = r * k;
     if (l < k) {
-      if (l < cnt) {
+      if (l < cnt && a.in) {
         a.out_idx[ob + l] = (int32_t)(col_of(acc) + a.col_base);
-        a.out_val[ob + l] = value_bits(acc, row);
+        a.out_val[ob + l] = value_bits(acc, a.in + r * a.stride);
+      } else if (l < cnt) {
+        a.out_idx[ob + l] = (int32_t)(signed_col(acc) + a.col_base);
+        a.out_val[ob + l] = signed_value_bits(acc);
       } else {
         a.out_idx[ob + l] = TK_FILL_IDX;
         a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;
@@ -891,11 +893,8 @@ __global__ __launch_bounds__(kWgThreads) void shard_merge_kernel(ShardMergeArgs 
   const int64_t ob = r * k;
   if (l < k) {
     if (l < cnt) {
-      const uint32_t key = (uint32_t)(acc >> 32);
-      const uint32_t lo = (uint32_t)acc;
-      a.out_idx[ob + l] = (int32_t)(0x7FFFFFFFu - (lo >> 1));
-      a.out_val[ob + l] = (uint16_t)(key > 0x8000u ? key - 0x8000u
-                                                   : (key < 0x8000u ? 0x8000u | (0x8000u - key) : (lo & 1u) << 15));
+      a.out_idx[ob + l] = signed_col(acc);
+      a.out_val[ob + l] = signed_value_bits(acc);
     } else {
       a.out_idx[ob + l] = TK_FILL_IDX;
       a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;

@@ -57,7 +57,34 @@ struct ArgmaxArgs {
 
 hipError_t launch_argmax(const ArgmaxArgs &a, int64_t rows_in_launch, hipStream_t stream);
 
+// Fused draft head (tk_head.hip): one workgroup per span of kHeadSpanCols
+// vocabulary columns (spans = ceil(vocab / kHeadSpanCols)); each writes, for
+// every row, the span's top k as signed composites (key << 32 |
+// (0x7FFFFFFF - column) << 1 | sign) into span_list [rows][spans][k] with
+// counts and flags [rows][spans], for span_merge_kernel (in == NULL) to fold.
+// logits: NULL, or [rows][logits_stride] bf16 to receive the logits as well.
+struct HeadArgs {
+  int64_t rows;
+  int64_t hidden;
+  int64_t vocab;
+  int32_t k;
+  int32_t spans;
+  const uint16_t *h;
+  int64_t h_stride;
+  const uint16_t *w;
+  int64_t w_stride;
+  uint64_t *span_list;
+  int32_t *span_count;
+  uint32_t *span_flags;
+  uint16_t *logits;
+  int64_t logits_stride;
+};
+
+hipError_t launch_head_scan(const HeadArgs &a, hipStream_t stream);
+
 // One merge workgroup per (row, group of up to kMergeGroup input lists).
+// With in == NULL the lists hold signed composites (see HeadArgs) and the
+// outputs are decoded from them alone.
 // With lists_out == 1 the merge writes the final outputs.
 struct MergeArgs {
   const uint16_t *in;  // the input matrix: entry values are read back from it

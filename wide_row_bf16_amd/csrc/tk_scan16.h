@@ -173,3 +173,16 @@ __device__ __forceinline__ int count_beating(const uint64_t *list, int n, uint64
   }
   return lo;
 }
+
+// Signed composites key << 32 | (0x7FFFFFFF - column) << 1 | sign: the same
+// order as the plain ones for distinct columns, and the value's sign bit
+// carried along, so an entry's bits come back without the input (-0 and +0
+// share a key).
+__device__ __forceinline__ int32_t signed_col(uint64_t x) { return (int32_t)(0x7FFFFFFFu - ((uint32_t)x >> 1)); }
+
+__device__ __forceinline__ uint16_t signed_value_bits(uint64_t x) {
+  const uint32_t key = (uint32_t)(x >> 32);
+  if (key > 0x8000u) return (uint16_t)(key - 0x8000u);
+  if (key < 0x8000u) return (uint16_t)(0x8000u | (0x8000u - key));
+  return (uint16_t)(((uint32_t)x & 1u) << 15);
+}
