@@ -42,7 +42,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kWgWaves;
-constexpr int kHeadUnroll = 2;  // hidden steps of 32 per register group (two groups in flight)
 static_assert(kHeadTilesPerWave == 4, "each wave owns four 16-column tiles");
 static_assert(kHeadSpanCols <= 8 * kWave, "a row's span fits eight columns per lane");
 
@@ -59,56 +58,41 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Fragments of kHeadUnroll hidden steps: B of this wave's four column tiles
-// (w) and A of each 16-row tile (h).
-template <int RT>
-struct HeadFrags {
-  bf16x8 b[kHeadUnroll][kHeadTilesPerWave];
-  bf16x8 a[kHeadUnroll][RT];
-};
-
 // An offset past every descriptor's range (ranges stay below 2^30 bytes and
 // the per-lane offsets below 2^30 too, so the sum cannot wrap): such a load
-// returns zeros.
+// returns zeros.  Used instead of branches around loads, which would make the
+// compiler wait for every outstanding load at the join.
 constexpr uint32_t kHeadPastEnd = 0x7FFFFFF0u;
 
-// Loads hidden steps [s0, s0 + kHeadUnroll); steps at or past `steps` read
-// zeros through an out-of-range offset instead of a branch, so that the
-// compiler keeps the other group's loads in flight (a conditional load makes
-// it wait for every outstanding load at the join).  w is read with the
-// default cache policy: a 128-byte line of a w row is split between two
-// consecutive steps, and nontemporal loads measured ~10% slower here.
-template <int RT>
-__device__ __forceinline__ void head_load(HeadFrags<RT> &F, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rh,
-                                          uint32_t b_off, uint32_t b_tile, uint32_t a_off, uint32_t a_tile, int s0,
-                                          int steps) {
-#pragma unroll
-  for (int u = 0; u < kHeadUnroll; ++u) {
-    const bool in = s0 + u < steps;
-    const uint32_t koff = (uint32_t)(s0 + u) * 64u;
-#pragma unroll
-    for (int j = 0; j < kHeadTilesPerWave; ++j)
-      F.b[u][j] = load_frag<0>(rw, in ? b_off + j * b_tile + koff : kHeadPastEnd);
-#pragma unroll
-    for (int t = 0; t < RT; ++t) F.a[u][t] = load_frag<0>(rh, in ? a_off + t * a_tile + koff : kHeadPastEnd);
-  }
-}
+// w is staged through LDS in blocks of kHeadBlockBytes per row of the wave's
+// 64 rows: each load instruction reads whole cache lines of a few rows (16
+// bytes per lane), the block is written to the wave's own LDS region with a
+// row pitch 16 bytes longer than the block, and the matrix-core
+// fragments (16 bytes of one row per lane) are read back from there.  Loaded
+// straight in the fragment layout, every line would be split over two
+// 64-byte requests of two instructions; measured 3.1 TB/s that way.
+constexpr int kHeadBlockBytes = 128;                            // per row and block
+constexpr int kHeadRowPitch = kHeadBlockBytes + 16;             // +16: conflict-free fragment reads
+constexpr int kHeadWaveRows = kHeadTilesPerWave * 16;           // 64 rows of w per wave
+constexpr int kHeadLanesPerRow = kHeadBlockBytes / 16;          // lanes of one load on one row
+constexpr int kHeadRowsPerLoad = kWave / kHeadLanesPerRow;      // rows of one load instruction
+constexpr int kHeadBlockLoads = kHeadWaveRows / kHeadRowsPerLoad;
+constexpr int kHeadBlockSteps = kHeadBlockBytes / 64;           // hidden steps of 32 per block
+static_assert(kHeadBlockBytes % 128 == 0 && kHeadWaveRows % kHeadRowsPerLoad == 0, "whole lines per row");
 
-// Steps past the end hold zeros and add nothing.
+struct HeadBlock {
+  u32x4 v[kHeadBlockLoads];
+};
+
 template <int RT>
-__device__ __forceinline__ void head_mma(f32x4 (&acc)[kHeadTilesPerWave][RT], const HeadFrags<RT> &F) {
-#pragma unroll
-  for (int u = 0; u < kHeadUnroll; ++u)
-#pragma unroll
-    for (int j = 0; j < kHeadTilesPerWave; ++j)
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F.a[u][t], F.b[u][j], acc[j][t], 0, 0, 0);
-}
+struct HeadA {
+  bf16x8 a[kHeadBlockSteps][RT];
+};
 
 template <int RT>
 __global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
   __shared__ uint16_t s_logit[RT * 16][kHeadSpanCols];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[kWgWaves][kHeadWaveRows * kHeadRowPitch];
 
   const int s = blockIdx.x;
   const int64_t n0 = (int64_t)s * kHeadSpanCols;
@@ -128,22 +112,81 @@ __global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int tile0 = wave * kHeadTilesPerWave;
-  const uint32_t b_off = (uint32_t)(((int64_t)(tile0 * 16 + l % 16) * a.w_stride + 8 * (l / 16)) * 2);
-  const uint32_t b_tile = (uint32_t)(16 * a.w_stride * 2);
+  const int64_t hidden_bytes = a.hidden * 2;
+  const int nblk = (int)((hidden_bytes + kHeadBlockBytes - 1) / kHeadBlockBytes);
+  // block loads: instruction q reads kHeadRowsPerLoad wave rows, lane l row
+  // q * kHeadRowsPerLoad + l / kHeadLanesPerRow, bytes 16 (l % kHeadLanesPerRow)
+  const int lrow = l / kHeadLanesPerRow, lbyte = 16 * (l % kHeadLanesPerRow);
+  const uint32_t g_lane = (uint32_t)(((int64_t)(tile0 * 16 + lrow) * a.w_stride) * 2 + lbyte);
+  const uint32_t g_q = (uint32_t)(kHeadRowsPerLoad * a.w_stride * 2);
+  uint8_t *lds_w = s_w[wave];
+  const uint32_t st_lane = (uint32_t)(lrow * kHeadRowPitch + lbyte);
+  const uint32_t ld_lane = (uint32_t)((l % 16) * kHeadRowPitch + 16 * (l / 16));
   const uint32_t a_off = (uint32_t)(((int64_t)(l % 16) * a.h_stride + 8 * (l / 16)) * 2);
   const uint32_t a_tile = (uint32_t)(16 * a.h_stride * 2);
-  const int steps = (int)(a.hidden / 32);
 
-  // Two register groups of kHeadUnroll hidden steps each: the loads of one
-  // group are in flight while the other's matrix-core work runs.
-  HeadFrags<RT> F0, F1;
-  head_load<RT>(F0, rw, rh, b_off, b_tile, a_off, a_tile, 0, steps);
-  for (int s0 = 0; s0 < steps; s0 += 2 * kHeadUnroll) {
-    head_load<RT>(F1, rw, rh, b_off, b_tile, a_off, a_tile, s0 + kHeadUnroll, steps);
-    head_mma<RT>(acc, F0);
-    if (s0 + kHeadUnroll >= steps) break;
-    head_load<RT>(F0, rw, rh, b_off, b_tile, a_off, a_tile, s0 + 2 * kHeadUnroll, steps);
-    head_mma<RT>(acc, F1);
+  // Loads are unconditional (a branch around them makes the compiler wait for
+  // every outstanding load at the join); the bytes of a block past `hidden`
+  // -- the next row's, or zeros past the buffer's range -- are zeroed in
+  // registers, and blocks past the last are loaded but never used.
+  auto load_block = [&](HeadBlock &B, int blk) {
+    const bool in = (int64_t)blk * kHeadBlockBytes + lbyte < hidden_bytes;
+#pragma unroll
+    for (int q = 0; q < kHeadBlockLoads; ++q) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, (int)(g_lane + q * g_q + (uint32_t)blk * kHeadBlockBytes), 0, 0);
+      B.v[q] = in ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto load_a = [&](HeadA<RT> &A, int blk) {
+#pragma unroll
+    for (int t = 0; t < kHeadBlockSteps; ++t) {
+      const int step = kHeadBlockSteps * blk + t;
+      const bool in = (int64_t)step * 64 < hidden_bytes;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        A.a[t][r] = load_frag<0>(rh, in ? a_off + r * a_tile + (uint32_t)step * 64u : kHeadPastEnd);
+    }
+  };
+  auto store_block = [&](const HeadBlock &B) {
+#pragma unroll
+    for (int q = 0; q < kHeadBlockLoads; ++q)
+      *reinterpret_cast<u32x4 *>(lds_w + st_lane + q * kHeadRowsPerLoad * kHeadRowPitch) = B.v[q];
+  };
+  auto mma_block = [&](const HeadA<RT> &A) {
+#pragma unroll
+    for (int t = 0; t < kHeadBlockSteps; ++t)
+#pragma unroll
+      for (int j = 0; j < kHeadTilesPerWave; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(lds_w + ld_lane + j * 16 * kHeadRowPitch + 64 * t);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[j][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.a[t][r], b, acc[j][r], 0, 0, 0);
+      }
+  };
+
+  // Block blk is in LDS while block blk + 1 is in registers (in flight) and
+  // the h fragments of the next block load.  LDS serves a wave's operations
+  // in order, so storing the next block after this block's fragment reads
+  // needs no barrier (the region is the wave's own).
+  HeadBlock Bn;
+  HeadA<RT> A0, A1;
+  load_block(Bn, 0);
+  load_a(A0, 0);
+  store_block(Bn);
+  load_block(Bn, 1);
+  load_a(A1, 1);
+  for (int blk = 0; blk < nblk; blk += 2) {
+    mma_block(A0);
+    if (blk + 1 >= nblk) break;
+    store_block(Bn);
+    load_block(Bn, blk + 2);
+    load_a(A0, blk + 2);
+    mma_block(A1);
+    if (blk + 2 >= nblk) break;
+    store_block(Bn);
+    load_block(Bn, blk + 3);
+    load_a(A1, blk + 3);
   }
 
   // accumulators -> bf16 logits in LDS (and, on request, to memory)
