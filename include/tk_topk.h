@@ -106,10 +106,11 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
  *          otherwise skip elements below a floor estimated from a sample and
  *          verify it afterwards, scanning again when it does not hold).
  *   general  0 = automatic; 1 = k == 1 runs the general top-k scan instead of
- *          the argmax scan (the control of that fast path).  bf16 and fp16
- *          only; fp32 rows accept it and always run their general scan.
- *          With k == 1 the argmax scan takes spans (forced or planned) up to
- *          64; above that the general scan runs.
+ *          the argmax scan (the control of that fast path), for every input
+ *          format.  Automatically k == 1 takes the argmax scan when rows are
+ *          fewer than the GPU's CUs or spans is forced, else the general scan.  With k == 1 the argmax scan takes spans (forced or
+ *          planned) up to 64; above that (bf16 / fp16 only) the general scan
+ *          runs.
  *   Values other than 0 and 1 for exact and general give TK_ERR_OPTION.
  */
 typedef struct tk_options {

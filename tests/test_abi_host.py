@@ -124,6 +124,15 @@ def test_plan_k1():
             assert rows < 256 or s == max(1, -(-(cols // 8) // 32640))  # only the span width limit
 
 
+def test_option_general_accepted_for_every_format():
+    import ctypes
+
+    lib = tk.load()
+    for fmt in ("bf16", "f16", "f32"):
+        fn = getattr(lib, f"tk_topk_{fmt}_ex")
+        assert fn(0, 100, 100, 1, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(tk.TkOptions(general=1))) == OK
+
+
 def test_plan_large_k():
     # k > 64: the k <= 64 plan, at most 8 spans unless the span width needs more
     assert tk.plan_spans(1024, 151936, 128) == 1

@@ -161,3 +161,6 @@ def test_configs(name):
     log(f"{name} k=1")
     assert_same(gpu_topk(m, cfg.cols, 1, x=x), want, f"{name} k=1")
     assert_same(control(x, cfg.cols), want, f"{name} k=1 general")
+    # a forced plan always takes the argmax scan (with a row per CU the
+    # automatic plan takes the general one)
+    assert_same(gpu_topk(m, cfg.cols, 1, spans=1, x=x), want, f"{name} k=1 argmax spans=1")

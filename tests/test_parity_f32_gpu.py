@@ -84,3 +84,57 @@ def test_equal_negative_rows_with_partial_waves():
                 log(f"f32 equal negative cols={cols} v={v} k={k}")
                 check_case(m, cols, k, spans=1, what=f"f32 equal {v} cols={cols} k={k}", fmt="f32")
                 check_case(m, cols, k, what=f"f32 equal {v} cols={cols} k={k} auto", fmt="f32")
+
+
+def test_split_rows_beyond_one_batch_and_state_f32():
+    """4100 split fp32 rows: two launches of the fused fold share the arrival
+    counters (zero again after every row), then other split shapes on the
+    same stream."""
+    cols = 2112
+    m = family_rows("logit", 4100, cols, cols, seed=17, fmt="f32")
+    want = oracle.topk_f32(m, cols, 24)
+    x = upload(m)
+    for spans in (2, 1, 3, 2):
+        log(f"f32 4100 rows spans={spans}")
+        assert_same(gpu_topk(m, cols, 24, spans=spans, x=x, fmt="f32"), want, f"f32 4100 rows spans={spans}")
+    for rows, c, k, spans in ((15, 98592, 32, 0), (3, 70000, 64, 64), (40, 9000, 8, 4)):
+        mm = family_rows("mixed_nonfinite", rows, c, c, seed=rows, fmt="f32")
+        log(f"f32 state rows={rows} cols={c} k={k} spans={spans}")
+        check_case(mm, c, k, spans=spans, what=f"f32 {rows}x{c} spans={spans}", fmt="f32")
+
+
+@pytest.mark.parametrize("family", sorted(FAMILIES))
+def test_argmax_f32(family):
+    """k = 1 on fp32 rows runs the argmax scan: the oracle's bytes, and the
+    same as the general scan (tk_options.general) over widths, strides,
+    misaligned rows and span counts."""
+    import wide_row_bf16_amd as tk
+    from gpu_util import to_numpy
+
+    fi = sorted(FAMILIES).index(family)
+    for i, w in enumerate([1, 3, 4, 5, 63, 1000, 4099, 16384, 98592, 151936]):
+        stride = [w, w + 1, w + 3][(i + fi) % 3]
+        spans = [0, 1, 2, 7, 64][(i + fi) % 5]
+        if spans > w:
+            spans = 0
+        offset = (i + fi) % 4
+        m = family_rows(family, 3, w, stride, seed=900 + 13 * fi + i, fmt="f32")
+        what = f"f32 k=1 family={family} cols={w} stride={stride} spans={spans} offset={offset}"
+        log(what)
+        want = oracle.topk_f32(m, w, 1)
+        x = upload(m, offset)
+        assert_same(to_numpy(tk.topk_f32(x, 1, cols=w, spans=spans)), want, what)
+        assert_same(to_numpy(tk.topk_f32(x, 1, cols=w, spans=spans, general=True)), want, what + " (general)")
+
+
+def test_argmax_f32_batches():
+    import wide_row_bf16_amd as tk
+    from gpu_util import to_numpy
+
+    cols = 4100
+    m = family_rows("normal", 4100, cols, cols, seed=23, fmt="f32")
+    want = oracle.topk_f32(m, cols, 1)
+    x = upload(m)
+    for spans in (2, 0, 1, 4):
+        log(f"f32 k=1 4100 rows spans={spans}")
+        assert_same(to_numpy(tk.topk_f32(x, 1, cols=cols, spans=spans)), want, f"f32 k=1 4100 rows spans={spans}")

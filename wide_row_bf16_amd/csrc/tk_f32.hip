@@ -145,10 +145,7 @@ struct Filter32 {
   uint32_t ftrip;    // patterns >= ftrip: -inf (0xFF800000) or negative NaN
 };
 
-__device__ __forceinline__ Filter32 make_filter32(const Wave32 &w) {
-  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(w.kth >> 32));
-  const uint32_t t = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
-  const uint32_t flags = (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags);
+__device__ __forceinline__ Filter32 filter32_for(uint32_t t, uint32_t flags) {
   Filter32 f;
   f.nonneg = t >= 0x80000000u;
   f.t32 = (int32_t)(t - 0x80000000u);
@@ -156,6 +153,12 @@ __device__ __forceinline__ Filter32 make_filter32(const Wave32 &w) {
   f.check_flags = (flags & (kNan | kNinf)) != (kNan | kNinf);
   f.ftrip = (flags & kNinf) ? 0xFF800001u : 0xFF800000u;
   return f;
+}
+
+__device__ __forceinline__ Filter32 make_filter32(const Wave32 &w) {
+  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(w.kth >> 32));
+  const uint32_t t = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
+  return filter32_for(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags));
 }
 
 __device__ __forceinline__ uint64_t value_trip(uint4 d, const Filter32 &f) {
@@ -522,11 +525,230 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k = 1 on fp32 rows: the argmax scan of the 16-bit formats (tk_kernels.hip)
+// with 32-bit keys -- one wave-uniform best composite (key << 32 | ~column,
+// absolute columns), T = max(its key, the other waves' published best keys
+// under the left/right rule), a tripped chunk costing one per-lane maximum
+// over the tripping vectors and one 64-bit wave maximum; split rows keep one
+// composite and one flags word per span for the row's last workgroup.
+
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v, const Xchg &x) {
+  uint64_t y;
+  y = partner64<1>(v, x); v = v > y ? v : y;
+  y = partner64<2>(v, x); v = v > y ? v : y;
+  y = partner64<4>(v, x); v = v > y ? v : y;
+  y = partner64<8>(v, x); v = v > y ? v : y;
+  y = partner64<16>(v, x); v = v > y ? v : y;
+  y = partner64<32>(v, x); v = v > y ? v : y;
+  return readlane64(v, 0);
+}
+
+struct WaveArgmax32 {
+  uint64_t best;    // wave-uniform best composite, 0 = none
+  uint32_t flags;   // wave-uniform NaN / -inf flags
+  int wave;
+  uint32_t *s_key;  // LDS: each wave's best key
+  Xchg x;
+};
+
+__device__ __forceinline__ uint32_t argmax_bound32(const WaveArgmax32 &w) {
+  uint32_t ext = 0;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    if (o == w.wave) continue;
+    const uint32_t t = __hip_atomic_load(&w.s_key[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ext = max(ext, o < w.wave ? t : (t > 0 ? t - 1 : 0u));
+  }
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ext);
+}
+
+__device__ __forceinline__ void argmax_update32(WaveArgmax32 &w, uint64_t m, bool nan, bool ninf) {
+  if (ballot(nan)) w.flags |= kNan;
+  if (ballot(ninf)) w.flags |= kNinf;
+  const uint64_t wm = wave_max64(m, w.x);
+  if (wm > w.best) {
+    w.best = wm;
+    if (lane_id() == 0)
+      __hip_atomic_store(&w.s_key[w.wave], (uint32_t)(wm >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// One chunk (lane l's vector u = first + 64 u + l, its element e at column
+// col_first + 4 (first + 64 u + l) + e).
+__device__ __forceinline__ void argmax_chunk32(WaveArgmax32 &w, const uint4 (&v)[kChunkVecs], uint32_t first,
+                                               uint32_t nvec, uint32_t col_first) {
+  const uint32_t t = max((uint32_t)(w.best >> 32), argmax_bound32(w));
+  const Filter32 f = filter32_for(t, w.flags);
+  const uint32_t l = (uint32_t)lane_id();
+  uint64_t trip[kChunkVecs], any = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    trip[u] = (value_trip(v[u], f) | flag_trip(v[u], f)) & lanes_ult(first + (uint32_t)(u * kWave) + l, nvec);
+    any |= trip[u];
+  }
+  if (!any) return;
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // rotated: no dynamic index into registers
+  uint64_t t0 = trip[0], t1 = trip[1], t2 = trip[2], t3 = trip[3];
+  uint32_t col = col_first + kElems32 * (first + l);
+  uint64_t m = 0;
+  bool nan = false, ninf = false;
+#pragma unroll 1
+  for (int u = 0; u < kChunkVecs; ++u) {
+    if ((t0 >> l) & 1u) {
+      const uint32_t dw[4] = {x0.x, x0.y, x0.z, x0.w};
+#pragma unroll
+      for (int e = 0; e < kElems32; ++e) {
+        const uint32_t key = key32(dw[e]);
+        nan |= key == 0;
+        ninf |= dw[e] == 0xFF800000u;
+        const uint64_t c = key ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (col + (uint32_t)e)) : 0;
+        m = m > c ? m : c;
+      }
+    }
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+    t0 = t1;
+    t1 = t2;
+    t2 = t3;
+    t3 = 0;
+    if (!(t0 | t1 | t2)) break;
+    col += kElems32 * kWave;
+  }
+  argmax_update32(w, m, nan, ninf);
+}
+
+__device__ void argmax_columns32(WaveArgmax32 &w, const uint32_t *row, int64_t lo, int64_t hi) {
+  uint64_t m = 0;
+  bool nan = false, ninf = false;
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? row[col] : 0u;
+    const uint32_t key = valid ? key32(b) : 0u;
+    nan |= valid && key == 0;
+    ninf |= valid && b == 0xFF800000u;
+    const uint64_t c = key ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (uint32_t)col) : 0;
+    m = m > c ? m : c;
+  }
+  argmax_update32(w, m, nan, ninf);
+}
+
+__global__ __launch_bounds__(kWgThreads) void argmax_scan32_kernel(ArgmaxArgs32 a) {
+  __shared__ uint32_t s_key[kWgWaves];
+  __shared__ uint64_t s_best[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const uint32_t *row = a.in + r * a.stride;
+
+  // the span and wave shares of span_scan32_kernel
+  const int64_t a0 = (int64_t)((4u - (uint32_t)(((uintptr_t)row >> 2) & 3u)) & 3u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kElems32 : 0;
+  int64_t j0 = 0, j1 = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kElems32 * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+
+  if (threadIdx.x < kWgWaves) s_key[threadIdx.x] = 0;
+  __syncthreads();
+  WaveArgmax32 w;
+  w.best = 0;
+  w.flags = 0;
+  w.wave = wave;
+  w.s_key = s_key;
+  w.x = make_xchg();
+
+  if (wave == 0 && head_hi > 0) argmax_columns32(w, row, 0, head_hi);
+  const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t nvec = (uint32_t)(wv1 - wv0);
+  if (nvec > 0) {
+    constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+    const uint32_t lane_off = (uint32_t)l * 16u;
+    const uint32_t col_first = (uint32_t)(a0 + kElems32 * wv0);
+    uint4 A[kChunkVecs], B[kChunkVecs];
+    load_chunk32(A, vp, nvec, 0, lane_off);
+    for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+      load_chunk32(B, vp, nvec, first + kStep, lane_off);
+      argmax_chunk32(w, A, first, nvec, col_first);
+      if (first + kStep >= nvec) break;
+      load_chunk32(A, vp, nvec, first + 2 * kStep, lane_off);
+      argmax_chunk32(w, B, first + kStep, nvec, col_first);
+    }
+  }
+  if (wave == kWgWaves - 1 && tail_hi > tail_lo) argmax_columns32(w, row, tail_lo, tail_hi);
+
+  if (l == 0) {
+    s_best[wave] = w.best;
+    s_fl[wave] = w.flags;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  uint64_t best = 0;
+  uint32_t fl = 0;
+#pragma unroll
+  for (int o = 0; o < kWgWaves; ++o) {
+    best = best > s_best[o] ? best : s_best[o];
+    fl |= s_fl[o];
+  }
+  if (S > 1) {
+    const int64_t rb = r - a.row0;
+    if (l == 0) {
+      __hip_atomic_store(&a.span_slot[rb * S + s], best, __ATOMIC_RELAXED, kAgent);
+      __hip_atomic_store(&a.span_flag[rb * S + s], fl, __ATOMIC_RELAXED, kAgent);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    int last = 0;
+    if (l == 0) last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
+    if (!ballot(last)) return;
+    const uint64_t v = l < S ? __hip_atomic_load(&a.span_slot[rb * S + l], __ATOMIC_RELAXED, kAgent) : 0;
+    const uint32_t f = l < S ? __hip_atomic_load(&a.span_flag[rb * S + l], __ATOMIC_RELAXED, kAgent) : 0u;
+    fl = (ballot(f & kNan) ? kNan : 0u) | (ballot(f & kNinf) ? kNinf : 0u);
+    best = wave_max64(v, make_xchg());
+    if (l == 0) __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
+  }
+  if (l == 0) {
+    if ((uint32_t)(best >> 32) == 0x80000000u + 0x7F800000u) fl |= kPinf;
+    if (best) {
+      a.out_idx[r] = col_of32(best);
+      a.out_val[r] = value_bits32(best, row);
+    } else {
+      a.out_idx[r] = TK_FILL_IDX;
+      a.out_val[r] = 0x7FC00000u;
+    }
+    a.out_count[r] = best ? 1 : 0;
+    a.out_nonfinite[r] = fl;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
   const int64_t blocks = rows_in_launch * a.spans;
   hipLaunchKernelGGL(span_scan32_kernel, dim3((uint32_t)blocks), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
+  if (rows_in_launch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_scan32_kernel, dim3((uint32_t)(rows_in_launch * a.spans)), dim3(kWgThreads), 0, stream, a);
   return hipGetLastError();
 }
 

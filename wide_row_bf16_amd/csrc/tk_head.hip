@@ -41,7 +41,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kWgWaves;
+constexpr int kHeadWaves = kHeadSpanCols / 64;                  // waves per workgroup (four tiles each)
+constexpr int kHeadThreads = kHeadWaves * kWave;
+constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kHeadWaves;
 static_assert(kHeadTilesPerWave == 4, "each wave owns four 16-column tiles");
 static_assert(kHeadSpanCols <= 8 * kWave, "a row's span fits eight columns per lane");
 
@@ -90,9 +92,9 @@ struct HeadA {
 };
 
 template <int RT>
-__global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
+__global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
   __shared__ uint16_t s_logit[RT * 16][kHeadSpanCols];
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[kWgWaves][kHeadWaveRows * kHeadRowPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[kHeadWaves][kHeadWaveRows * kHeadRowPitch];
 
   const int s = blockIdx.x;
   const int64_t n0 = (int64_t)s * kHeadSpanCols;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
   // per row: the span's top k (8 columns per lane, as one vector of the scans)
   const Xchg x = make_xchg();
   const int k = a.k;
-  for (int row = wave; row < a.rows; row += kWgWaves) {
+  for (int row = wave; row < a.rows; row += kHeadWaves) {
     uint32_t c[8];
     bool nan = false, ninf = false;
 #pragma unroll
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kWgThreads) void head_scan_kernel(HeadArgs a) {
 
 hipError_t launch_head_scan(const HeadArgs &a, hipStream_t stream) {
   if (a.rows <= 0 || a.spans <= 0) return hipSuccess;
-  const dim3 grid((uint32_t)a.spans), block(kWgThreads);
+  const dim3 grid((uint32_t)a.spans), block(kHeadThreads);
   if (a.rows <= 16) {
     hipLaunchKernelGGL(head_scan_kernel<1>, grid, block, 0, stream, a);
   } else if (a.rows <= 32) {

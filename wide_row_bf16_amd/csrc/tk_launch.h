@@ -174,6 +174,26 @@ struct ScanArgs32 {
 };
 
 hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
+
+// k = 1 on fp32 rows (tk_f32.hip), as ArgmaxArgs with 32-bit inputs and
+// values; split rows keep a composite (key << 32 | ~column) and a flags word
+// per span.
+struct ArgmaxArgs32 {
+  const uint32_t *in;
+  int64_t row0;
+  int64_t cols;
+  int64_t stride;
+  int32_t spans;
+  uint64_t *span_slot;  // [rows_in_launch][spans]
+  uint32_t *span_flag;  // [rows_in_launch][spans]
+  int32_t *row_done;
+  int32_t *out_idx;
+  uint32_t *out_val;
+  int32_t *out_count;
+  uint32_t *out_nonfinite;
+};
+
+hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
 
