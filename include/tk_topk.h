@@ -38,9 +38,9 @@
  * every call.
  *
  * k up to 64 keeps one wavefront lane per entry; 64 < k <= TK_MAX_K (256)
- * runs a scan whose per-wave kept list spans two or four registers (bf16 and
- * fp16 rows; the pages give the library a compile-time max_k, and this is
- * its extension).  fp32 rows, the shard merge and sampling take k <=
+ * runs a scan whose per-wave kept list spans two or four registers (every
+ * input format; the pages give the library a compile-time max_k, and this is
+ * its extension).  The shard merge, sampling and the fused head take k <=
  * TK_MAX_K_LANE (64).
  *
  * Errors: the guards below run on the host before any device work; on a
@@ -57,8 +57,8 @@
 extern "C" {
 #endif
 
-#define TK_MAX_K 256u     /* largest k of tk_topk_bf16 / tk_topk_f16 (and their _ex, _shard forms) */
-#define TK_MAX_K_LANE 64u /* largest k of fp32 rows, the shard merge and sampling: one lane per entry */
+#define TK_MAX_K 256u     /* largest k of the row top-k (bf16, fp16, fp32; _ex and _shard forms) */
+#define TK_MAX_K_LANE 64u /* largest k of the shard merge, sampling and the fused head: one lane per entry */
 
 #define TK_NONFINITE_NAN 1u    /* the row has at least one NaN (none is an entry)  */
 #define TK_NONFINITE_POSINF 2u /* the row has at least one +inf                    */
@@ -144,7 +144,7 @@ tk_status tk_topk_f16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
  * aligned, row_stride in elements; out_val: uint32 [rows][k], the entries'
  * own bits, empty slots 0x7FC00000.  Keys are 32 bits wide and composites 64,
  * so one span may be any width; tk_options.spans accepts 0..64
- * (TK_ERR_OPTION above).  1 <= k <= TK_MAX_K_LANE (TK_ERR_K above).
+ * (TK_ERR_OPTION above).  1 <= k <= TK_MAX_K (TK_ERR_K above).
  * tk_validate_f32 gives the guards alone.
  */
 tk_status tk_topk_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,

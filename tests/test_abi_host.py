@@ -163,7 +163,12 @@ def test_option_fields(fmt):
     assert ctypes.sizeof(tk.TkOptions) == 32
     assert call() == OK and call(general=1) == OK and call(exact=1, general=1, spans=4) == OK
     assert call(general=2) == OPTION and call(general=-1) == OPTION and call(exact=2) == OPTION
-    if fmt != "f32":
+    if fmt == "f32":
+        def wide32(spans):
+            return fn(0, 100000, 100000, 65, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(tk.TkOptions(spans=spans)))
+
+        assert wide32(64) == OK and wide32(65) == OPTION
+    else:
         # k > 64: at most 64 spans, forced or needed by the width
         def wide(spans, cols):
             return fn(0, cols, cols, 65, IN, IDX, VAL, CNT, MSK, 0, ctypes.byref(tk.TkOptions(spans=spans)))
@@ -250,7 +255,7 @@ def test_f32_guards():
     assert v32(i=IN + 2) == ALIGN and v32(val=VAL + 2) == ALIGN  # 4-byte elements
     assert v32(i=IN + 4) == OK
     assert v32(k=0) == K and v32(stride=99) == SHAPE
-    assert v32(k=64) == OK and v32(k=65) == K  # fp32 rows keep one lane per entry
+    assert v32(k=64) == OK and v32(k=256) == OK and v32(k=257) == K
     # the input spans 4 bytes per element: an output 1000 bytes in overlaps it
     assert v32(idx=IN + 1000) == ALIAS
     assert tk.validate(3, 100, 100, 8, IN, IN + 1000, VAL, CNT, MSK) == OK  # bf16: 600 bytes of input only

@@ -138,3 +138,50 @@ def test_argmax_f32_batches():
     for spans in (2, 0, 1, 4):
         log(f"f32 k=1 4100 rows spans={spans}")
         assert_same(to_numpy(tk.topk_f32(x, 1, cols=cols, spans=spans)), want, f"f32 k=1 4100 rows spans={spans}")
+
+
+@pytest.mark.parametrize("family", sorted(FAMILIES))
+def test_wide_k_f32(family):
+    """64 < k <= 256 on fp32 rows (the multi-register scan): the oracle's
+    bytes over widths, strides, misaligned rows and span counts."""
+    fi = sorted(FAMILIES).index(family)
+    for i, w in enumerate([1, 9, 65, 257, 1000, 4103, 70000, 151936]):
+        stride = [w, w + 1, w + 3][(i + fi) % 3]
+        k = [65, 100, 128, 129, 200, 256][(i + 2 * fi) % 6]
+        spans = [0, 1, 2, 8, 64][(i + fi) % 5]
+        if spans > w:
+            spans = 0
+        offset = (i + fi) % 4
+        m = family_rows(family, 2, w, stride, seed=4000 + 7 * fi + i, fmt="f32")
+        what = f"f32 wide family={family} cols={w} stride={stride} k={k} spans={spans} offset={offset}"
+        log(what)
+        check_case(m, w, k, spans=spans, offset=offset, what=what, fmt="f32")
+
+
+@pytest.mark.parametrize("family", ["ascending", "normal", "few_levels", "posinf_many"])
+def test_wide_k_f32_speculation_and_batches(family):
+    cols = 151936
+    m = family_rows(family, 3, cols, cols, seed=len(family), fmt="f32")
+    x = upload(m)
+    for k in (65, 200):
+        want = oracle.topk_f32(m, cols, k)
+        for exact in (False, True):
+            log(f"f32 wide speculate family={family} k={k} exact={exact}")
+            assert_same(gpu_topk(m, cols, k, x=x, fmt="f32", exact=exact), want, f"{family} k={k} exact={exact}")
+    if family == "normal":
+        mm = family_rows("logit", 4100, 1100, 1100, seed=5, fmt="f32")
+        want = oracle.topk_f32(mm, 1100, 128)
+        xx = upload(mm)
+        for spans in (2, 1, 2):
+            log(f"f32 wide 4100 rows spans={spans}")
+            assert_same(gpu_topk(mm, 1100, 128, spans=spans, x=xx, fmt="f32"), want, f"f32 wide 4100 spans={spans}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_wide_k_f32_configs(name):
+    cfg = CONFIGS[name]
+    m = bf16_to_f32_bits(make_config_input(name), np.random.default_rng(3))
+    x = upload(m)
+    for k in (128, 256):
+        log(f"f32 wide {name} k={k}")
+        assert_same(gpu_topk(m, cfg.cols, k, x=x, fmt="f32"), oracle.topk_f32(m, cfg.cols, k), f"f32 {name} k={k}")

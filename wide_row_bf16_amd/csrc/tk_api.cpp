@@ -801,7 +801,7 @@ tk_status run_argmax32(int64_t rows, int64_t cols, int64_t stride, const uint32_
 tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint32_t *in, int32_t *out_idx,
                 uint32_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
                 const tk_options *opt) {
-  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxK);
+  tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxKWide);
   if (st != TK_OK) return st;
   int32_t forced = 0, exact = 0, general = 0;
   if (opt) {
@@ -824,6 +824,10 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
                         forced > 0 ? forced : plan_argmax32(rows, cols, device_cus(dev)));
   int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
   if (spans > kMergeGroup) spans = kMergeGroup;
+  if (k > kMaxK && forced == 0 && spans > kWideMaxAutoSpans) spans = kWideMaxAutoSpans;
+  // k > 64: the multi-register scan, with the same arguments and scratch
+  hipError_t (*const launch)(const tk::ScanArgs32 &, int64_t, hipStream_t) =
+      k > kMaxK ? tk::launch_wide_scan32 : tk::launch_span_scan32;
 
   tk::ScanArgs32 sa{};
   sa.in = in;
@@ -843,7 +847,7 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
       const int64_t nr = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
       sa.row0 = r0;
-      if (tk::launch_span_scan32(sa, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
+      if (launch(sa, nr, stream) != hipSuccess) return TK_ERR_DEVICE;
     }
     return TK_OK;
   }
@@ -883,7 +887,7 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
     b.out_val = out_val + r0 * k;
     b.out_count = out_count + r0;
     b.out_nonfinite = out_nonfinite + r0;
-    if (tk::launch_span_scan32(b, nr, stream) != hipSuccess) {
+    if (launch(b, nr, stream) != hipSuccess) {
       result = TK_ERR_DEVICE;
       break;
     }
@@ -933,7 +937,7 @@ tk_status tk_topk_f32_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t
 tk_status tk_validate_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint32_t *in,
                           const int32_t *out_idx, const uint32_t *out_val, const int32_t *out_count,
                           const uint32_t *out_nonfinite) {
-  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxK);
+  return guard(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, 4, kMaxKWide);
 }
 
 tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,

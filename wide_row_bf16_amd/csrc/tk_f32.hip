@@ -30,17 +30,15 @@ namespace tk {
 namespace {
 
 #include "tk_wave.h"
+#include "tk_lists.h"
 
 constexpr int kElems32 = 4;  // fp32 per 16-byte vector
+constexpr int kWideSpecChunks32 = 4;  // k > 64: a speculative floor needs this many chunks per wave
 
 __device__ __forceinline__ uint32_t key32(uint32_t b) {
   const uint32_t mag = b & 0x7FFFFFFFu;
   const uint32_t key = (b & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
   return mag > 0x7F800000u ? 0u : key;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  return ((uint64_t)readlane((uint32_t)(v >> 32), l) << 32) | readlane((uint32_t)v, l);
 }
 
 __device__ __forceinline__ uint64_t lanes_ugt64(uint64_t a, uint64_t b) { return ballot(a > b); }
@@ -738,6 +736,372 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan32_kernel(ArgmaxArgs32 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64 < k <= 256 on fp32 rows: the multi-register scan of tk_wide.hip with the
+// 64-bit composites of this file -- each wave keeps 64 R composites (R = 2 or
+// 4 registers of 64 bits, tk_lists.h), filters on raw bits (Filter32), takes
+// the pooled exact and verified speculative floors, shares thresholds, merges
+// the four lists by rank in LDS, and folds split rows in their last
+// workgroup.
+
+template <int R>
+struct WaveWide32 {
+  uint64_t L[R];
+  uint64_t kth;    // wave-uniform copy of rank k - 1
+  uint32_t ext;    // wave-uniform: keys <= ext are beaten by k entries of the workgroup (or the floor)
+  uint32_t floor;
+  uint32_t flags;
+  int km1, qm1, wave;
+  uint32_t *tau;
+  Xchg x;
+};
+
+template <int R>
+__device__ __forceinline__ void wide32_offer(WaveWide32<R> &w, uint64_t c, uint64_t m) {
+  if (__popcll(m) >= kBatchInsert) {
+    const bool take = (m >> lane_id()) & 1ull;
+    wide_merge_batch64<R>(w.L, take ? c : 0, w.x);
+  } else {
+    do {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      wide_insert_one64<R>(w.L, readlane64(c, l));
+    } while (m);
+  }
+  w.kth = wide_at64<R>(w.L, w.km1);
+}
+
+template <int R>
+__device__ __forceinline__ void wide32_publish(const WaveWide32<R> &w) {
+  const uint32_t q = (uint32_t)(readlane64(w.L[0], w.qm1) >> 32);
+  if (lane_id() == 0) {
+    __hip_atomic_store(&w.tau[w.wave], (uint32_t)(w.kth >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&w.tau[kWgWaves + w.wave], q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// One vector of four elements per lane (lanes `lanes`), element by element
+// (a runtime loop rotating the words keeps one copy of the insertion code).
+template <int R>
+__device__ __forceinline__ void wide32_vector(WaveWide32<R> &w, uint4 d, uint32_t col0, uint64_t lanes) {
+#pragma unroll 1
+  for (int e = 0; e < kElems32; ++e) {
+    const uint32_t b = d.x;
+    d = make_uint4(d.y, d.z, d.w, d.x);
+    const uint32_t key = key32(b);
+    if (lanes & ballot(key == 0)) w.flags |= kNan;
+    if (lanes & ballot(b == 0xFF800000u)) w.flags |= kNinf;
+    const uint64_t c = key > w.ext ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e)) : 0;
+    const uint64_t m = lanes & lanes_ugt64(c, w.kth);
+    if (m) wide32_offer<R>(w, c, m);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void wide32_chunk(WaveWide32<R> &w, const uint4 (&v)[kChunkVecs], uint32_t first,
+                                             uint32_t nvec, uint32_t col_first) {
+  w.ext = max(shared_bound32(w.tau, w.wave), w.floor);
+  const Filter32 f = filter32_for(max((uint32_t)(w.kth >> 32), w.ext), w.flags);
+  const uint32_t l = (uint32_t)lane_id();
+  uint64_t trip[kChunkVecs], any = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    trip[u] = (value_trip(v[u], f) | flag_trip(v[u], f)) & lanes_ult(first + (uint32_t)(u * kWave) + l, nvec);
+    any |= trip[u];
+  }
+  if (!any) return;
+  uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  uint64_t t0 = trip[0], t1 = trip[1], t2 = trip[2], t3 = trip[3];
+  uint32_t col = col_first + kElems32 * (first + l);
+#pragma unroll 1
+  for (int u = 0; u < kChunkVecs; ++u) {
+    if (t0) wide32_vector<R>(w, x0, col, t0);
+    x0 = x1;
+    x1 = x2;
+    x2 = x3;
+    t0 = t1;
+    t1 = t2;
+    t2 = t3;
+    t3 = 0;
+    if (!(t0 | t1 | t2)) break;
+    col += kElems32 * kWave;
+  }
+  wide32_publish<R>(w);
+}
+
+template <int R>
+__device__ __forceinline__ void wide32_body(WaveWide32<R> &w, const uint4 *vp, uint32_t nvec, uint32_t col_first,
+                                            uint4 (&A)[kChunkVecs]) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+  const uint32_t lane_off = (uint32_t)lane_id() * 16u;
+  uint4 B[kChunkVecs];
+  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;  // progress priority, as take_body32
+  __builtin_amdgcn_s_setprio(3);
+  for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
+    if (first >= q3) __builtin_amdgcn_s_setprio(0);
+    else if (first >= q2) __builtin_amdgcn_s_setprio(1);
+    else if (first >= q1) __builtin_amdgcn_s_setprio(2);
+    load_chunk32(B, vp, nvec, first + kStep, lane_off);
+    wide32_chunk<R>(w, A, first, nvec, col_first);
+    if (first + kStep >= nvec) break;
+    load_chunk32(A, vp, nvec, first + 2 * kStep, lane_off);
+    wide32_chunk<R>(w, B, first + kStep, nvec, col_first);
+  }
+}
+
+template <int R>
+__device__ void wide32_columns(WaveWide32<R> &w, const uint32_t *row, int64_t lo, int64_t hi) {
+  for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+    const int64_t col = c0 + lane_id();
+    const bool valid = col < hi;
+    const uint32_t b = valid ? row[col] : 0u;
+    const uint32_t key = key32(b);
+    if (ballot(valid && key == 0)) w.flags |= kNan;
+    if (ballot(valid && b == 0xFF800000u)) w.flags |= kNinf;
+    const uint64_t c = (valid && key > w.ext) ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (uint32_t)col) : 0;
+    const uint64_t m = lanes_ugt64(c, w.kth);
+    if (m) wide32_offer<R>(w, c, m);
+  }
+}
+
+// Last-workgroup fold of a split row (the protocol of fold_row32_if_last),
+// lists of up to 64 R entries merged as R-register lists.
+template <int R>
+__device__ __forceinline__ void wide32_fold_if_last(const ScanArgs32 &a, int64_t r, int S, const uint32_t *row,
+                                                    int wave, int l, uint64_t (*s_acc)[kWave * R]) {
+  __shared__ int s_last;
+  __shared__ int32_t s_cnt[kWgWaves];
+  __shared__ uint32_t s_fl[kWgWaves];
+  const int64_t rb = r - a.row0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  const Xchg x = make_xchg();
+  const int k = a.k;
+  uint64_t acc[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = 0;
+  int cnt = 0;
+  uint32_t fl = 0;
+  for (int i = wave; i < S; i += kWgWaves) {
+    const int64_t sb = r * S + i;
+    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent);
+    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
+    uint64_t B[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = j * kWave + l;
+      B[j] = e < c ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+    }
+    cnt += c;
+    if (i == wave) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] = B[j];
+    } else {
+      wide_merge_lists64<R>(acc, B, x);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) s_acc[wave][j * kWave + l] = acc[j];
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_fl[wave] = fl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int step = 1; step < kWgWaves; step *= 2) {
+    if (wave % (2 * step) == 0) {
+      uint64_t B[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) B[j] = s_acc[wave + step][j * kWave + l];
+      wide_merge_lists64<R>(acc, B, x);
+#pragma unroll
+      for (int j = 0; j < R; ++j) s_acc[wave][j * kWave + l] = acc[j];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+#pragma unroll
+  for (int o = 1; o < kWgWaves; ++o) {
+    cnt += s_cnt[o];
+    fl |= s_fl[o];
+  }
+  if (cnt > k) cnt = k;
+  const int64_t ob = r * k;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int e = j * kWave + l;
+    if (e < k) {
+      if (e < cnt) {
+        a.out_idx[ob + e] = col_of32(acc[j]);
+        a.out_val[ob + e] = value_bits32(acc[j], row);
+      } else {
+        a.out_idx[ob + e] = TK_FILL_IDX;
+        a.out_val[ob + e] = 0x7FC00000u;
+      }
+    }
+  }
+  if (l == 0) {
+    a.out_count[r] = cnt;
+    a.out_nonfinite[r] = fl;
+    __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
+  __shared__ uint64_t s_list[kWgWaves][kWave * R];
+  __shared__ int32_t s_count[kWgWaves];
+  __shared__ uint32_t s_flags[kWgWaves];
+  __shared__ uint32_t s_tau[2 * kWgWaves];
+  __shared__ uint32_t s_samp[kWgWaves][kWave];
+
+  const int64_t blk = blockIdx.x;
+  const int64_t r = a.row0 + blk / a.spans;
+  const int s = (int)(blk % a.spans);
+  const int S = a.spans;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int l = lane_id();
+  const uint32_t *row = a.in + r * a.stride;
+
+  // the span and wave shares of span_scan32_kernel
+  const int64_t a0 = (int64_t)((4u - (uint32_t)(((uintptr_t)row >> 2) & 3u)) & 3u);
+  const int64_t nv_row = a.cols > a0 ? (a.cols - a0) / kElems32 : 0;
+  int64_t j0 = 0, j1 = 0, head_hi = 0, tail_lo = 0, tail_hi = 0;
+  if (nv_row > 0) {
+    j0 = nv_row * s / S;
+    j1 = nv_row * (s + 1) / S;
+    if (s == 0) head_hi = a0;
+    if (s == S - 1) {
+      tail_lo = a0 + kElems32 * nv_row;
+      tail_hi = a.cols;
+    }
+  } else if (s == 0) {
+    head_hi = a.cols;
+  }
+  const int64_t n = j1 - j0;
+  const int64_t wv0 = j0 + n * wave / kWgWaves;
+  const int64_t wv1 = j0 + n * (wave + 1) / kWgWaves;
+  const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
+  const uint32_t wn = (uint32_t)(wv1 - wv0);
+
+  // floors from the workgroup's 256 first-chunk lane maxima (R-register merge:
+  // k may exceed one register)
+  const Xchg x = make_xchg();
+  uint4 A[kChunkVecs];
+  if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
+  s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key32(A, wn) : 0u, x);
+  __syncthreads();
+  uint32_t exact_floor, spec_floor = 0;
+  {
+    uint32_t P[R];
+    P[0] = s_samp[0][l];
+#pragma unroll
+    for (int j = 1; j < R; ++j) P[j] = 0;
+#pragma unroll
+    for (int o = 1; o < kWgWaves; ++o) wide_merge_batch<R>(P, s_samp[o][l], x);
+    const uint32_t te = wide_at<R>(P, a.k - 1);
+    exact_floor = te > 0 ? te - 1 : 0;
+    if (a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks32 * kChunkVecs * kWave) {
+      const uint32_t ts = wide_at<R>(P, a.spec_rank - 1);
+      spec_floor = ts > 0 ? ts - 1 : 0;
+    }
+  }
+  uint32_t floor = exact_floor;
+  bool verify = false;
+  if (spec_floor > exact_floor) {
+    floor = spec_floor;
+    verify = true;
+  }
+
+  WaveWide32<R> w;
+  int total = 0;
+  uint32_t flags = 0;
+  for (;;) {
+    if (threadIdx.x < 2 * kWgWaves) s_tau[threadIdx.x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < R; ++j) w.L[j] = 0;
+    w.kth = 0;
+    w.ext = floor;
+    w.floor = floor;
+    w.flags = 0;
+    w.km1 = a.k - 1;
+    w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
+    w.wave = wave;
+    w.tau = s_tau;
+    w.x = x;
+
+    if (wave == 0 && head_hi > 0) wide32_columns<R>(w, row, 0, head_hi);
+    if (wn > 0) wide32_body<R>(w, wvp, wn, (uint32_t)(a0 + kElems32 * wv0), A);
+    if (wave == kWgWaves - 1 && tail_hi > tail_lo) wide32_columns<R>(w, row, tail_lo, tail_hi);
+
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      s_list[wave][j * kWave + l] = w.L[j];
+      cnt += __popcll(ballot(w.L[j] != 0));
+    }
+    if (l == 0) {
+      s_count[wave] = cnt < a.k ? cnt : a.k;
+      s_flags[wave] = w.flags | ((uint32_t)(readlane64(w.L[0], 0) >> 32) == 0xFF800000u ? kPinf : 0u);
+    }
+    __syncthreads();
+    total = 0;
+    flags = 0;
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o) {
+      total += s_count[o];
+      flags |= s_flags[o];
+    }
+    if (!verify || total >= a.k) break;  // exact, or the speculation verified
+    floor = exact_floor;
+    verify = false;
+    if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
+    __syncthreads();
+  }
+  if (total > a.k) total = a.k;
+
+  const int64_t sb = r * S + s;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int e = j * kWave + l;
+    if (e >= s_count[wave]) continue;
+    const uint64_t xv = s_list[wave][e];
+    int rank = e;
+#pragma unroll
+    for (int o = 0; o < kWgWaves; ++o)
+      if (o != wave) rank += count_beating32(s_list[o], s_count[o], xv);
+    if (rank >= a.k) continue;
+    if (S == 1) {
+      a.out_idx[r * a.k + rank] = col_of32(xv);
+      a.out_val[r * a.k + rank] = value_bits32(xv, row);
+    } else {
+      __hip_atomic_store(&a.span_list[sb * a.k + rank], xv, __ATOMIC_RELAXED, kAgent);
+    }
+  }
+  if (S == 1) {
+    const int t = threadIdx.x;
+    if (t >= total && t < a.k) {
+      a.out_idx[r * a.k + t] = TK_FILL_IDX;
+      a.out_val[r * a.k + t] = 0x7FC00000u;
+    }
+    if (t == 0) {
+      a.out_count[r] = total;
+      a.out_nonfinite[r] = flags;
+    }
+    return;
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
+    __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
+  }
+  __syncthreads();  // the rank merge's reads of s_list are done; the fold reuses it
+  wide32_fold_if_last<R>(a, r, S, row, wave, l, s_list);
+}
+
 }  // namespace
 
 hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
@@ -749,6 +1113,17 @@ hipError_t launch_span_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipSt
 hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
   if (rows_in_launch <= 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_scan32_kernel, dim3((uint32_t)(rows_in_launch * a.spans)), dim3(kWgThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wide_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream) {
+  if (rows_in_launch <= 0) return hipSuccess;
+  const dim3 grid((uint32_t)(rows_in_launch * a.spans)), block(kWgThreads);
+  if (a.k <= 2 * kWave) {
+    hipLaunchKernelGGL(wide_scan32_kernel<2>, grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(wide_scan32_kernel<4>, grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

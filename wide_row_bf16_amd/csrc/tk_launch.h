@@ -194,6 +194,10 @@ struct ArgmaxArgs32 {
 };
 
 hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
+
+// 64 < k <= 256 on fp32 rows (tk_f32.hip): ScanArgs32 as for
+// launch_span_scan32 (split rows folded by their last workgroup).
+hipError_t launch_wide_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
 

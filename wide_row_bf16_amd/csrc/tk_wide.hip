@@ -37,6 +37,7 @@ namespace {
 
 #include "tk_wave.h"
 #include "tk_scan16.h"
+#include "tk_lists.h"
 
 // A speculative floor is tried only when each wave's share spans at least this
 // many chunks (shorter shares are mostly sample already).
@@ -44,46 +45,6 @@ constexpr int kWideSpecChunks = 4;
 // This many tripping lanes in a vector take the dense path (all composites,
 // a per-lane sort, batch merges); fewer take the per-element lean path.
 constexpr int kWideDenseLanes = 16;
-
-// ---- R-register lists (32-bit in-wave composites) ----
-
-template <int R>
-__device__ __forceinline__ void wide_insert_one(uint32_t (&L)[R], uint32_t c) {
-  uint32_t carry[R];
-  carry[0] = 0xFFFFFFFFu;
-#pragma unroll
-  for (int j = 1; j < R; ++j) carry[j] = readlane(L[j - 1], kWave - 1);
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)carry[j], (int)L[j], 0x138, 0xF, 0xF, false);
-    L[j] = max(L[j], min(prev, c));
-  }
-}
-
-// Merges 64 candidates v (any order, 0 = none) into the list.
-template <int R>
-__device__ __forceinline__ void wide_merge_batch(uint32_t (&L)[R], uint32_t v, const Xchg &x) {
-  v = sort64_desc(v, x);
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (!ballot(v != 0)) break;
-    // the batch's best does not beat this register's last entry: it passes on whole
-    if (readlane(v, 0) <= readlane(L[j], kWave - 1)) continue;
-    const uint32_t rv = partner<63>(v, x);
-    const uint32_t hi = max(L[j], rv), lo = min(L[j], rv);
-    L[j] = bitonic_merge64_desc(hi, x);
-    if (j + 1 < R) v = bitonic_merge64_desc(lo, x);
-  }
-}
-
-template <int R>
-__device__ __forceinline__ uint32_t wide_at(const uint32_t (&L)[R], int rank) {
-  uint32_t v = 0;
-#pragma unroll
-  for (int j = 0; j < R; ++j)
-    if ((rank >> 6) == j) v = readlane(L[j], rank & (kWave - 1));
-  return v;
-}
 
 template <int R>
 struct WaveWide {
@@ -266,39 +227,6 @@ __device__ void wide_columns(WaveWide<R> &w, const uint16_t *row, int64_t lo, in
 }
 
 // ---- R-register lists of 64-bit composites (the fold of split rows) ----
-
-__device__ __forceinline__ uint64_t bitonic_merge64_u64(uint64_t v, const Xchg &x) {
-  v = cx_stage64<32, 32>(v, x);
-  v = cx_stage64<16, 16>(v, x);
-  v = cx_stage64<8, 8>(v, x);
-  v = cx_stage64<4, 4>(v, x);
-  v = cx_stage64<2, 2>(v, x);
-  v = cx_stage64<1, 1>(v, x);
-  return v;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  return ((uint64_t)readlane((uint32_t)(v >> 32), l) << 32) | readlane((uint32_t)v, l);
-}
-
-// Merges the sorted list B (R registers, descending, 0 = none) into A.
-template <int R>
-__device__ __forceinline__ void wide_merge_lists64(uint64_t (&A)[R], const uint64_t (&B)[R], const Xchg &x) {
-#pragma unroll
-  for (int jb = 0; jb < R; ++jb) {
-    uint64_t v = B[jb];
-    if (!ballot(v != 0)) break;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (!ballot(v != 0)) break;
-      if (readlane64(v, 0) <= readlane64(A[j], kWave - 1)) continue;
-      const uint64_t rv = partner64<63>(v, x);
-      const uint64_t hi = A[j] > rv ? A[j] : rv, lo = A[j] > rv ? rv : A[j];
-      A[j] = bitonic_merge64_u64(hi, x);
-      if (j + 1 < R) v = bitonic_merge64_u64(lo, x);
-    }
-  }
-}
 
 // Last-workgroup fold of a split row (the protocol of the k <= 64 scan):
 // arrival counted after the span's stores completed; the last arrival loads
