@@ -31,6 +31,8 @@ CASES = [
     (5, 64, 700, 16, 0, 0, "integers"),
     (40, 96, 1500, 33, 0, 0, "integers"),
     (9, 64, 500, 16, 0, 0, "nonfinite"),
+    (7, 2016, 3000, 24, 8, 8, "normal"),  # one row tile, 32 hidden blocks of which the last is half
+    (12, 1056, 2000, 32, 0, 0, "integers"),
     (15, 2048, 98592, 32, 0, 0, "normal"),
     (64, 1024, 151936, 8, 0, 0, "normal"),
 ]

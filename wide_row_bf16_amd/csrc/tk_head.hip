@@ -18,7 +18,8 @@
 // 32 hidden values of 16 vocabulary rows of w (each lane loads 16 contiguous
 // bytes of one w row: lane l takes row l % 16, values 8 (l / 16) .. + 7), one
 // accumulator per (column tile, row tile); the loads of the next hidden steps
-// are in flight while the current ones multiply.  w is read once; h is small
+// are in flight while the current ones multiply, and with one row tile each
+// span starts its walk over the hidden dimension at its own hashed block.  w is read once; h is small
 // and shared by every workgroup.  Buffer
 // descriptors clamp both: rows past vocab or past rows read zero.  The
 // accumulators are rounded to bf16 into LDS; then each wave takes rows w,
@@ -116,6 +117,19 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
   const int tile0 = wave * kHeadTilesPerWave;
   const int64_t hidden_bytes = a.hidden * 2;
   const int nblk = (int)((hidden_bytes + kHeadBlockBytes - 1) / kHeadBlockBytes);
+  // Logical block b reads hidden block (b + rot) mod nblk, rot hashed from the
+  // span.  Without it every wave of the grid reads the same block offset of
+  // rows w_stride apart at the same time: requests that share their low
+  // address bits and so crowd onto the same memory channels.  With one row
+  // tile (the memory-bound case) the rotation measured 117 -> 103 us on
+  // 15 x 2048 x 98592; with two or four row tiles it measured slower and is
+  // not used.  Only the order of the fp32 sums changes.
+  const int rot = RT == 1 ? (int)((((uint32_t)s * 2654435761u) >> 16) % (uint32_t)nblk) : 0;
+  auto phys = [&](int blk) {  // blocks past the last (loaded, never used) keep their index
+    if (blk >= nblk) return blk;
+    const int p = blk + rot;
+    return p >= nblk ? p - nblk : p;
+  };
   // block loads: instruction q reads kHeadRowsPerLoad wave rows, lane l row
   // q * kHeadRowsPerLoad + l / kHeadLanesPerRow, bytes 16 (l % kHeadLanesPerRow)
   const int lrow = l / kHeadLanesPerRow, lbyte = 16 * (l % kHeadLanesPerRow);
@@ -131,7 +145,8 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
   // every outstanding load at the join); the bytes of a block past `hidden`
   // -- the next row's, or zeros past the buffer's range -- are zeroed in
   // registers, and blocks past the last are loaded but never used.
-  auto load_block = [&](HeadBlock &B, int blk) {
+  auto load_block = [&](HeadBlock &B, int logical) {
+    const int blk = phys(logical);
     const bool in = (int64_t)blk * kHeadBlockBytes + lbyte < hidden_bytes;
 #pragma unroll
     for (int q = 0; q < kHeadBlockLoads; ++q) {
@@ -140,7 +155,8 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
       B.v[q] = in ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto load_a = [&](HeadA<RT> &A, int blk) {
+  auto load_a = [&](HeadA<RT> &A, int logical) {
+    const int blk = phys(logical);
 #pragma unroll
     for (int t = 0; t < kHeadBlockSteps; ++t) {
       const int step = kHeadBlockSteps * blk + t;
