@@ -21,7 +21,7 @@ constexpr int64_t kMaxWaveCols = 65536;        // a wave's relative column fits 
 constexpr int64_t kMaxSpanVecs = 32640;        // 16-byte vectors one workgroup scans at most
 constexpr int64_t kMaxSpanCols = kMaxSpanVecs * kVecElems;  // 261120
 constexpr int kMergeGroup = 64;                // span lists one merge workgroup folds at most
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;              // sixteen waves: four lists each, then a tree over the waves
 constexpr int kFusedMaxRows = 4096;             // rows per launch of the fused (single-dispatch) split path
 constexpr int kBatchInsert = 8;                // >= this many new candidates: bitonic batch merge
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays

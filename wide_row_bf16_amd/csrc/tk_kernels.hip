@@ -766,7 +766,8 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan_kernel(ArgmaxArgs a) {
 // threads first stage the group's lists in LDS (every load in flight at
 // once), then each wave folds its share pairwise in registers (lane j holds
 // entry j) with bitonic merges of the 64-bit composites -- the same (score
-// desc, column asc) order as the scan -- and wave 0 folds the four results.
+// desc, column asc) order as the scan -- and the waves' results meet in a
+// tree through LDS.
 __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
   constexpr int kWaves = kMergeThreads / kWave;
   __shared__ uint64_t s_lists[kMergeGroup * kMaxK];
@@ -805,15 +806,21 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
     acc = li == wave ? v : merge_sorted64(acc, v, x);
     cnt += c;
   }
+  // the waves' results meet as a tree: at step w, wave i (a multiple of 2w)
+  // takes the merge of its result and wave i + w's
   s_acc[wave][l] = acc;
   if (l == 0) s_cnt[wave] = cnt;
-  __syncthreads();
-  if (wave != 0) return;
 #pragma unroll
-  for (int o = 1; o < kWaves; ++o) {
-    acc = merge_sorted64(acc, s_acc[o][l], x);
-    cnt += s_cnt[o];
+  for (int w = 1; w < kWaves; w *= 2) {
+    __syncthreads();
+    if ((wave & (2 * w - 1)) == 0) {
+      acc = merge_sorted64(acc, s_acc[wave + w][l], x);
+      cnt += s_cnt[wave + w];
+      s_acc[wave][l] = acc;
+      if (l == 0) s_cnt[wave] = cnt;
+    }
   }
+  if (wave != 0) return;
   if (cnt > k) cnt = k;
   const uint32_t flags = s_flags;
 
