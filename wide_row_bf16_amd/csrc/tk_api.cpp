@@ -305,7 +305,7 @@ tk_status acquire_scratch(int dev, hipStream_t stream, size_t total, char **base
   *owned = scratch == nullptr;
   if (*owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
   if ((*owned || fresh) && tk::launch_zero_fill((int32_t *)scratch, kFusedMaxRows, stream) != hipSuccess) {
-    if (*owned) hipFreeAsync(scratch, stream);
+    if (*owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
     return TK_ERR_DEVICE;
   }
   *base = (char *)scratch;
@@ -665,7 +665,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   char *base = (char *)scratch;
   int32_t *counters = (int32_t *)base;
   if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
-    if (owned) hipFreeAsync(scratch, stream);
+    if (owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
     return TK_ERR_DEVICE;
   }
 
@@ -870,7 +870,7 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
   char *base = (char *)scratch;
   int32_t *counters = (int32_t *)base;
   if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
-    if (owned) hipFreeAsync(scratch, stream);
+    if (owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
     return TK_ERR_DEVICE;
   }
   tk_status result = TK_OK;

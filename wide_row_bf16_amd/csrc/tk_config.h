@@ -41,6 +41,5 @@ static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
 static_assert(((kMaxSpanVecs + kWgWaves - 1) / kWgWaves) * kVecElems + 2 * kVecElems <= kMaxWaveCols,
               "a wave's column range must fit the 16-bit relative index");
 static_assert(kSampleElems == kWgWaves * kChunkVecs * kWave * kVecElems, "sample = one chunk per wave");
-static_assert(kMergeGroup * kMaxK * 8 * 2 <= 64 * 1024, "merge double buffer must fit LDS");
 
 }  // namespace tk

@@ -762,19 +762,18 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan_kernel(ArgmaxArgs a) {
   }
 }
 
-// Folds up to kMergeGroup sorted candidate lists of one row into one.  All
-// threads first stage the group's lists in LDS (every load in flight at
-// once), then each wave folds its share pairwise in registers (lane j holds
-// entry j) with bitonic merges of the 64-bit composites -- the same (score
-// desc, column asc) order as the scan -- and the waves' results meet in a
-// tree through LDS.
+// Folds up to kMergeGroup sorted candidate lists of one row into one.  Each
+// wave loads its share of the lists straight into registers (lane j holds
+// entry j; every load in flight at once) and folds them pairwise with bitonic
+// merges of the 64-bit composites -- the same (score desc, column asc) order
+// as the scan; the waves' results then meet in a tree through LDS.
 __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
   constexpr int kWaves = kMergeThreads / kWave;
-  __shared__ uint64_t s_lists[kMergeGroup * kMaxK];
-  __shared__ int32_t s_count[kMergeGroup];
+  constexpr int kPerWave = kMergeGroup / kWaves;  // lists one wave folds
+  static_assert(kMergeGroup % kWaves == 0, "lists per wave");
   __shared__ uint64_t s_acc[kWaves][kWave];
   __shared__ int32_t s_cnt[kWaves];
-  __shared__ uint32_t s_flags;
+  __shared__ uint32_t s_fl[kWaves];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.lists_out;
@@ -783,46 +782,59 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
   int n = a.lists_in - first;
   if (n > a.group) n = a.group;
   const int k = a.k;
-  const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const Xchg x = make_xchg();
   const int64_t in_base = r * a.lists_in + first;
 
-  if (t == 0) s_flags = 0;
-  __syncthreads();
-  for (int i = t; i < n * k; i += kMergeThreads) s_lists[i] = a.list_in[in_base * k + i];
-  for (int i = t; i < n; i += kMergeThreads) {
-    s_count[i] = a.count_in[in_base + i];
-    atomicOr(&s_flags, a.flags_in[in_base + i]);
+  uint64_t v[kPerWave];
+  int c[kPerWave];
+  uint32_t fl = 0;
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int li = wave + j * kWaves;
+    c[j] = 0;
+    v[j] = 0;
+    if (li < n) {
+      c[j] = a.count_in[in_base + li];
+      fl |= a.flags_in[in_base + li];
+      if (l < k) v[j] = a.list_in[(in_base + li) * k + l];
+    }
   }
-  __syncthreads();
-
   uint64_t acc = 0;
   int cnt = 0;
-  for (int li = wave; li < n; li += kWaves) {
-    const int c = s_count[li];
-    const uint64_t v = l < c ? s_lists[li * k + l] : 0;
-    acc = li == wave ? v : merge_sorted64(acc, v, x);
-    cnt += c;
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    if (wave + j * kWaves >= n) break;
+    const uint64_t vj = l < c[j] ? v[j] : 0;
+    acc = j == 0 ? vj : merge_sorted64(acc, vj, x);
+    cnt += c[j];
   }
+
   // the waves' results meet as a tree: at step w, wave i (a multiple of 2w)
   // takes the merge of its result and wave i + w's
   s_acc[wave][l] = acc;
-  if (l == 0) s_cnt[wave] = cnt;
+  if (l == 0) {
+    s_cnt[wave] = cnt;
+    s_fl[wave] = fl;
+  }
 #pragma unroll
   for (int w = 1; w < kWaves; w *= 2) {
     __syncthreads();
     if ((wave & (2 * w - 1)) == 0) {
       acc = merge_sorted64(acc, s_acc[wave + w][l], x);
       cnt += s_cnt[wave + w];
+      fl |= s_fl[wave + w];
       s_acc[wave][l] = acc;
-      if (l == 0) s_cnt[wave] = cnt;
+      if (l == 0) {
+        s_cnt[wave] = cnt;
+        s_fl[wave] = fl;
+      }
     }
   }
   if (wave != 0) return;
   if (cnt > k) cnt = k;
-  const uint32_t flags = s_flags;
+  const uint32_t flags = fl;
 
   if (a.lists_out == 1) {
     const int64_t ob = r * k;
