@@ -89,6 +89,26 @@ def test_tiny_rows_all_k():
             check_case(m, w, k, what=f"tiny cols={w} k={k}")
 
 
+def test_merge_dispatch_levels():
+    """Forced span counts above the fused limit (64 spans) go through the merge
+    dispatch, levels of up to 64 lists per workgroup: one full and one ragged
+    group (65, 100), exact multiples (128), a group of one list (129), many
+    groups (1000), and three levels (5000 spans of ~20 columns) -- for k from
+    1 to 64, on ties, non-finite values and plain logits."""
+    cases = [
+        ("logit", 3, 98592, 20, 65),
+        ("mixed_nonfinite", 2, 98592, 64, 100),
+        ("levels64", 2, 98592, 1, 128),
+        ("few_levels", 2, 98592, 33, 129),
+        ("zeros_straddle", 2, 151936, 16, 1000),
+        ("normal", 2, 100000, 64, 5000),
+    ]
+    for family, rows, cols, k, spans in cases:
+        m = family_rows(family, rows, cols, cols + 5, seed=spans)
+        log(f"merge levels family={family} rows={rows} cols={cols} k={k} spans={spans}")
+        check_case(m, cols, k, spans=spans, what=f"merge levels {family} k={k} spans={spans}")
+
+
 def test_wide_rows_need_several_spans():
     """Rows wider than one workgroup's span limit, and a two-level merge."""
     for family in ("normal", "uniform_bits", "levels64"):

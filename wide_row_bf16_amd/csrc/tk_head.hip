@@ -46,7 +46,8 @@ constexpr int kHeadWaves = kHeadSpanCols / 64;                  // waves per wor
 constexpr int kHeadThreads = kHeadWaves * kWave;
 constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kHeadWaves;
 static_assert(kHeadTilesPerWave == 4, "each wave owns four 16-column tiles");
-static_assert(kHeadSpanCols <= 8 * kWave, "a row's span fits eight columns per lane");
+constexpr int kHeadLaneCols = 4;                               // a row's span: four columns per lane
+static_assert(kHeadSpanCols <= kHeadLaneCols * kWave, "a row's span fits four columns per lane");
 
 template <int POLICY>
 __device__ __forceinline__ bf16x8 load_frag(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
@@ -223,15 +224,17 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
   }
   __syncthreads();
 
-  // per row: the span's top k (8 columns per lane, as one vector of the scans)
+  // per row: the span's top k, four columns per lane (every lane busy): each
+  // lane sorts its four, then position by position the lanes' p-th best are
+  // merged in while any beats the k-th kept entry
   const Xchg x = make_xchg();
   const int k = a.k;
   for (int row = wave; row < a.rows; row += kHeadWaves) {
-    uint32_t c[8];
+    uint32_t c[kHeadLaneCols];
     bool nan = false, ninf = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 8 * l + e;
+    for (int e = 0; e < kHeadLaneCols; ++e) {
+      const int col = kHeadLaneCols * l + e;
       const bool valid = col < nvalid;
       const uint32_t b = valid ? (uint32_t)s_logit[row][col] : 0u;
       const uint32_t key = order_key(b);
@@ -240,10 +243,10 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
       c[e] = (valid && key) ? (key << 16) | (0xFFFFu - (uint32_t)col) : 0u;
     }
     uint32_t flags = (ballot(nan) ? kNan : 0u) | (ballot(ninf) ? kNinf : 0u);
-    sort8_desc(c);
+    cx(c[0], c[1]); cx(c[2], c[3]); cx(c[0], c[2]); cx(c[1], c[3]); cx(c[1], c[2]);  // descending
     uint32_t list = 0, kth = 0;
 #pragma unroll 1
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < kHeadLaneCols; ++p) {
       uint64_t m = lanes_ugt(c[0], kth);
       if (!m) break;
       if (__popcll(m) >= kBatchInsert) {
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
         } while (m);
       }
       kth = readlane(list, k - 1);
-      c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7]; c[7] = 0;
+      c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = 0;
     }
     const int cnt = min(__popcll(ballot(list != 0)), k);
     if ((readlane(list, 0) >> 16) == 0xFF80u) flags |= kPinf;
