@@ -93,8 +93,14 @@ struct HeadA {
   bf16x8 a[kHeadBlockSteps][RT];
 };
 
+// With four row tiles the kernel asks for two workgroups per CU: left alone the
+// compiler keeps the accumulators in AGPRs beside 182 VGPRs (310 registers, one
+// wave per SIMD), so only 256 of the 386 workgroups of a 98592-column head fit
+// and the grid ran in two rounds; under the bound it uses 243 VGPRs without
+// spills and 64 rows went from 185 to 160 us.  The same bound made two row
+// tiles slower (122 -> 146 us), so those kernels keep the default.
 template <int RT>
-__global__ __launch_bounds__(kHeadThreads) void head_scan_kernel(HeadArgs a) {
+__global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kernel(HeadArgs a) {
   __shared__ uint16_t s_logit[RT * 16][kHeadSpanCols];
   __shared__ __attribute__((aligned(16))) uint8_t s_w[kHeadWaves][kHeadWaveRows * kHeadRowPitch];
 
