@@ -46,7 +46,7 @@ def test_split_and_exact_f16(family):
     x = upload(m)
     for k in (1, 20, 64):
         want = oracle.topk_f16(m, cols, k)
-        for spans in (1, 2, 7, 12, 64):
+        for spans in (1, 2, 7, 12, 64, 65, 130):  # above 64: the merge dispatch
             log(f"f16 split family={family} k={k} spans={spans}")
             assert_same(gpu_topk(m, cols, k, spans=spans, x=x, fmt="f16"), want, f"{family} k={k} spans={spans}")
         assert_same(gpu_topk(m, cols, k, spans=1, x=x, fmt="f16", exact=True), want, f"{family} k={k} exact")
