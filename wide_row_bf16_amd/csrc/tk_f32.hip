@@ -260,13 +260,14 @@ __device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkV
 
 // Streams nvec vectors from vp (element 0 is column col_first), two chunks in
 // flight; A holds the first chunk, already loaded.  Issue priority falls
-// with progress, as in the bf16 scan.
+// with progress, as in the bf16 scan (steps at 1/2, 3/4 and 9/10 of the
+// share: 0.7 us faster than every quarter on 1024 x 151936 fp32 rows).
 __device__ __forceinline__ void take_body32(Wave32 &w, const uint4 *vp, uint32_t nvec, uint32_t col_first,
                                             uint4 (&A)[kChunkVecs]) {
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
   const uint32_t lane_off = (uint32_t)lane_id() * 16u;
   uint4 B[kChunkVecs];
-  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;
+  const uint32_t q1 = nvec / 2, q2 = nvec - nvec / 4, q3 = nvec - nvec / 10;
   __builtin_amdgcn_s_setprio(3);
   for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
     if (first >= q3) __builtin_amdgcn_s_setprio(0);
@@ -835,7 +836,9 @@ __device__ __forceinline__ void wide32_body(WaveWide32<R> &w, const uint4 *vp, u
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
   const uint32_t lane_off = (uint32_t)lane_id() * 16u;
   uint4 B[kChunkVecs];
-  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;  // progress priority, as take_body32
+  // progress priority in quarters: the steps of take_body32 measured 0.7 us
+  // slower here on 1024 x 151936 fp32 rows at k = 128
+  const uint32_t q1 = nvec / 4, q2 = nvec / 2, q3 = nvec - nvec / 4;
   __builtin_amdgcn_s_setprio(3);
   for (uint32_t first = 0; first < nvec; first += 2 * kStep) {
     if (first >= q3) __builtin_amdgcn_s_setprio(0);
