@@ -413,7 +413,16 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       const uint32_t lane_off = (uint32_t)l * 16u;
       const int64_t col_first = a0 + kVecElems * wv0;
       uint4 B[kChunkVecs];
+      // progress-based issue priority, as in the k <= 64 scan (waves that are
+      // behind issue first), here in quarters of the share: on 1024 x 151936
+      // rows it took k = 128 from 68.1 to 62.4 us and k = 256 from 96.9 to
+      // 85.2 us; steps at 1/2, 3/4, 9/10 measured 0.1-0.7 us slower
+      const uint32_t q1 = wn / 4, q2 = wn / 2, q3 = wn - wn / 4;
+      __builtin_amdgcn_s_setprio(3);
       for (uint32_t first = 0; first < wn; first += 2 * kStep) {
+        if (first >= q3) __builtin_amdgcn_s_setprio(0);
+        else if (first >= q2) __builtin_amdgcn_s_setprio(1);
+        else if (first >= q1) __builtin_amdgcn_s_setprio(2);
         load_chunk(B, wvp, wn, first + kStep, lane_off);
         wide_chunk<R>(w, A, first, wn, col_first, base);
         if (first + kStep >= wn) break;
