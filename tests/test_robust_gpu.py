@@ -142,3 +142,37 @@ def test_fused_merge_state_across_calls_and_batches():
 
         for _ in range(2):
             assert_same(gpu_topk(m, cols, k, spans=spans), want, f"{family} {rows}x{cols} k={k} spans={spans}")
+
+
+def test_library_loaded_before_torch():
+    """A caller that loads the library before importing torch must get working
+    calls: the binding imports torch before opening the library, so both use
+    the HIP runtime torch brings (a second, system runtime beside it made
+    every call fail with TK_ERR_DEVICE).  Runs in a fresh process, since this
+    one has torch loaded already."""
+    import json
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys, json\n"
+        f"sys.path.insert(0, {root!r})\n"
+        "import wide_row_bf16_amd as tk\n"
+        "tk.load()\n"
+        "import numpy as np, torch\n"
+        "from synth import family_rows\n"
+        "m = family_rows('mixed_nonfinite', 3, 5000, 5003, seed=3)\n"
+        "x = torch.from_numpy(m.view(np.int16)).to('cuda')\n"
+        "o = tk.topk_bf16(x, 16, cols=5000)\n"
+        "print(json.dumps([o.idx.cpu().tolist(), o.count.cpu().tolist()]))\n"
+    )
+    log("fresh process: library loaded before torch")
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    idx, count = json.loads(proc.stdout.strip().splitlines()[-1])
+    m = family_rows("mixed_nonfinite", 3, 5000, 5003, seed=3)
+    want = oracle.topk_bf16(m, 5000, 16)
+    assert np.array_equal(np.array(idx, dtype=np.int32), want[0])
+    assert np.array_equal(np.array(count, dtype=np.int32), want[2])

@@ -72,6 +72,14 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         from . import build as _build
 
         _build.build()
+    # PyTorch's ROCm wheel carries its own HIP runtime.  Opened first, this
+    # library would bind to the system runtime and torch would then map its
+    # own beside it: two runtimes in one process, where the device pointers
+    # and streams torch hands over are unknown to the runtime that launches
+    # these kernels (every call fails with TK_ERR_DEVICE).  Importing torch
+    # first makes the library bind to the runtime torch already loaded.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.tk_topk_bf16.restype = i32
