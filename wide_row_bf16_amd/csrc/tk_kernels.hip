@@ -888,25 +888,35 @@ __global__ __launch_bounds__(kWgThreads) void shard_merge_kernel(ShardMergeArgs 
   uint64_t acc = 0;
   int cnt = 0;
   uint32_t fl = 0;
-  for (int g0 = 0; g0 < a.shards; g0 += 4) {
-    uint64_t v[4];
-    int c[4];
+  // eight shards at a time, every load in flight at once: the entries are
+  // read whatever the count (the inputs are dense [shards][rows][k], fills
+  // past each count) and masked by it afterwards, so no load waits on another
+  constexpr int kShardBatch = 8;
+  for (int g0 = 0; g0 < a.shards; g0 += kShardBatch) {
+    uint32_t val[kShardBatch];
+    int32_t idx[kShardBatch];
+    int c[kShardBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // four shards' loads in flight
+    for (int j = 0; j < kShardBatch; ++j) {
       const int g = g0 + j;
       c[j] = 0;
-      v[j] = 0;
+      val[j] = 0;
+      idx[j] = 0;
       if (g < a.shards) {
         const int64_t sr = (int64_t)g * a.rows + r;
         c[j] = a.count_in[sr];
         fl |= a.mask_in[sr];
-        if (l < c[j] && l < k) v[j] = shard_composite(a.val_in[sr * k + l], a.idx_in[sr * k + l]);
+        if (l < k) {
+          val[j] = a.val_in[sr * k + l];
+          idx[j] = a.idx_in[sr * k + l];
+        }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kShardBatch; ++j) {
       if (g0 + j >= a.shards) break;
-      acc = (g0 == 0 && j == 0) ? v[j] : merge_sorted64(acc, v[j], x);
+      const uint64_t v = l < c[j] && l < k ? shard_composite(val[j], idx[j]) : 0;
+      acc = (g0 == 0 && j == 0) ? v : merge_sorted64(acc, v, x);
       cnt += c[j];
     }
   }
