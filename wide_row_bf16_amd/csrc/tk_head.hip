@@ -19,8 +19,8 @@
 // bytes of one w row: lane l takes row l % 16, values 8 (l / 16) .. + 7), one
 // accumulator per (column tile, row tile); the loads of the next hidden steps
 // are in flight while the current ones multiply, and with one row tile each
-// span starts its walk over the hidden dimension at its own hashed block.  w is read once; h is small
-// and shared by every workgroup.  Buffer
+// span starts its walk over the hidden dimension at its own hashed block.  w
+// is read once; h is small and shared by every workgroup.  Buffer
 // descriptors clamp both: rows past vocab or past rows read zero.  The
 // accumulators are rounded to bf16 into LDS; then each wave takes rows w,
 // w + 4, ... and keeps the span's top k of the row in one VGPR (lane i = i-th
@@ -48,6 +48,7 @@ constexpr int kHeadTilesPerWave = kHeadSpanCols / 16 / kHeadWaves;
 static_assert(kHeadTilesPerWave == 4, "each wave owns four 16-column tiles");
 constexpr int kHeadLaneCols = 4;                               // a row's span: four columns per lane
 static_assert(kHeadSpanCols <= kHeadLaneCols * kWave, "a row's span fits four columns per lane");
+static_assert(kHeadLaneCols == 4, "the per-lane sort and shift of the top-k are written for four");
 
 template <int POLICY>
 __device__ __forceinline__ bf16x8 load_frag(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
