@@ -888,9 +888,10 @@ __global__ __launch_bounds__(kWgThreads) void shard_merge_kernel(ShardMergeArgs 
   uint64_t acc = 0;
   int cnt = 0;
   uint32_t fl = 0;
-  // eight shards at a time, every load in flight at once: the entries are
-  // read whatever the count (the inputs are dense [shards][rows][k], fills
-  // past each count) and masked by it afterwards, so no load waits on another
+  // eight shards at a time, every load in flight at once: all k entries of a
+  // shard's row are read (the inputs are dense [shards][rows][k]) and those
+  // past its count, whatever they hold, are masked afterwards, so no load
+  // waits on another
   constexpr int kShardBatch = 8;
   for (int g0 = 0; g0 < a.shards; g0 += kShardBatch) {
     uint32_t val[kShardBatch];
