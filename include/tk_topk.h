@@ -79,7 +79,10 @@ typedef enum tk_status {
 } tk_status;
 
 /*
- * Row-wise exact top-k (see the file comment for the contract).
+ * Row-wise exact top-k (see the file comment for the contract): the wide-row
+ * top-k of TensorFold PR #713, change 3 (entries in score-then-lower-token
+ * order), with the outputs its Exactness table compares (entries, counts,
+ * non-finite masks).
  *   rows        >= 0; rows == 0 returns TK_OK without touching the device.
  *   cols        0 <= cols <= INT32_MAX; cols == 0 gives count 0 and all fills.
  *   row_stride  >= cols, in elements.
@@ -92,7 +95,11 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
 
 /*
  * Planning overrides, for tests and benchmarks.  The result never depends on
- * them: every plan computes the same bytes.
+ * them: every plan computes the same bytes.  TensorFold PR #713, change 3:
+ * its benchmark dispatches the single-group kernel directly as the control
+ * of the span path (spans = 1 here), and its Exactness table requires the
+ * span path's entries, counts and masks to equal that control's byte for
+ * byte (any spans here).
  *   spans  0 = automatic; 1 = one workgroup scans each whole row (the
  *          single-group control); n > 1 = split each row into n spans whose
  *          candidate lists are merged in the same order: by the row's last
@@ -158,7 +165,11 @@ tk_status tk_validate_f32(int64_t rows, int64_t cols, int64_t row_stride, int32_
 
 /*
  * The host-side guards alone (no HIP call is made): returns the status
- * tk_topk_bf16 would return before launching anything.
+ * tk_topk_bf16 would return before launching anything.  TensorFold PR #713,
+ * Exactness table, the row of the GPU top-k bench: the row ABI and its guards
+ * are checked beside the exact cases; this entry point lets a host test run
+ * every guard without a device.  Arguments as tk_topk_bf16 (no stream); the
+ * pointers are only compared, never dereferenced.
  */
 tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
                            const int32_t *out_idx, const uint16_t *out_val, const int32_t *out_count,
@@ -299,7 +310,15 @@ tk_status tk_validate_head_bf16(int64_t rows, int64_t hidden, int64_t vocab, int
                                 const uint16_t *out_val, const int32_t *out_count, const uint32_t *out_nonfinite,
                                 const uint16_t *logits, int64_t logits_stride);
 
-int32_t tk_max_k(void);             /* == TK_MAX_K */
+/*
+ * tk_max_k: TK_MAX_K, the largest k of the row top-k as built.  TensorFold PR
+ * #713, change 3 ties the kernel's lane, span and max_k constants to the
+ * calling side at compile time, so that a mismatch breaks the build; here the
+ * kernels' constants are static_asserted against this header's and the
+ * calling side reads the built value from the library (tk_max_span_cols
+ * likewise gives the widest span one workgroup scans).
+ */
+int32_t tk_max_k(void);
 int64_t tk_max_span_cols(void);     /* widest span one workgroup scans */
 const char *tk_status_string(tk_status s);
 const char *tk_build_info(void);    /* target and build flags of the library */

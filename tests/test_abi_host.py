@@ -289,4 +289,43 @@ def test_head_guards():
     assert vh(idx=W_FAKE + 1024) == ALIAS                  # an output inside the weights
     assert vh(lg=VAL - 64, ls=98592) == ALIAS               # logits over an output
     assert vh(cnt=MSK) == ALIAS
+    # logits rows are addressed in 64 bits: a stride that would overflow is rejected
+    assert vh(lg=0x60000000, ls=2**62) == SHAPE and vh(lg=0x60000000, ls=2**56) == SHAPE
+    assert vh(lg=0x60000000, ls=2**54 - 2**40) != SHAPE  # just inside the bound (then overlaps the outputs)
+
+
+def _cpu_out(torch, rows, k, val_dtype=None, **over):
+    val_dtype = torch.bfloat16 if val_dtype is None else val_dtype
+    t = {"idx": torch.empty((rows, k), dtype=torch.int32), "val": torch.empty((rows, k), dtype=val_dtype),
+         "count": torch.empty((rows,), dtype=torch.int32), "nonfinite": torch.empty((rows,), dtype=torch.int32)}
+    t.update(over)
+    return tk.TopK(t["idx"], t["val"], t["count"], t["nonfinite"])
+
+
+def test_binding_rejects_mismatched_out_tensors():
+    """Reused outputs of the wrong shape, dtype or layout would let the kernels
+    write past them; the binding's check raises before any call (CPU tensors,
+    the check alone)."""
+    import torch
+
+    cpu = torch.device("cpu")
+    tk._check_out(torch, _cpu_out(torch, 4, 8), 4, 8, "bf16", cpu)
+    tk._check_out(torch, _cpu_out(torch, 4, 8, torch.float32), 4, 8, "f32", cpu)
+    tk._check_out(torch, _cpu_out(torch, 4, 8, torch.float16), 4, 8, "f16", cpu)
+    bad = [
+        (_cpu_out(torch, 4, 4), 4, 8, "bf16"),                           # smaller k
+        (_cpu_out(torch, 2, 8), 4, 8, "bf16"),                           # fewer rows
+        (_cpu_out(torch, 4, 8), 4, 8, "f32"),                            # 2-byte values for 4-byte entries
+        (_cpu_out(torch, 4, 8, torch.float32), 4, 8, "bf16"),            # 4-byte values for bf16
+        (_cpu_out(torch, 4, 8, idx=torch.empty((4, 8), dtype=torch.int64)), 4, 8, "bf16"),
+        (_cpu_out(torch, 4, 8, idx=torch.empty((8, 4), dtype=torch.int32).t()), 4, 8, "bf16"),  # not contiguous
+        (_cpu_out(torch, 4, 8, count=torch.empty((5,), dtype=torch.int32)), 4, 8, "bf16"),
+        (_cpu_out(torch, 4, 8, nonfinite=torch.empty((4,), dtype=torch.int16)), 4, 8, "bf16"),
+        ((1, 2, 3), 4, 8, "bf16"),
+    ]
+    for out, rows, k, fmt in bad:
+        with pytest.raises(ValueError):
+            tk._check_out(torch, out, rows, k, fmt, cpu)
+    with pytest.raises(ValueError):  # outputs on another device than the input
+        tk._check_out(torch, _cpu_out(torch, 4, 8), 4, 8, "bf16", torch.device("cuda", 0))
 

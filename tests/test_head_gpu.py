@@ -110,3 +110,46 @@ def test_rejected_and_empty_calls():
     assert e.value.status == 2
     out = tk.head_topk_bf16(h[:0], w, 4)
     assert out.idx.shape == (0, 4)
+
+
+def test_wide_pads_on_tight_storage():
+    """Row pads wider than one 128-byte block of the kernel's walk, poisoned
+    with NaN, and w's storage ending at the last row's hidden-th element (no
+    pad after it): the loads past `hidden` must read nothing outside the
+    weights and use none of the pad."""
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    for rows, hidden, vocab, k, pad in ((15, 2048, 4000, 32, 136), (3, 96, 700, 16, 200), (33, 512, 1300, 20, 72)):
+        what = f"tight w storage rows={rows} hidden={hidden} vocab={vocab} pad={pad}"
+        log(what)
+        hb, wb = head_inputs(rows, hidden, vocab, seed=vocab + pad, h_pad=pad, w_pad=pad)
+        ws = hidden + pad
+        flat = np.ascontiguousarray(wb).reshape(-1)[: (vocab - 1) * ws + hidden]
+        wdev = torch.from_numpy(flat.view(np.int16).copy()).to("cuda")
+        w = wdev.as_strided((vocab, hidden), (ws, 1))
+        h = _dev(hb)[:, :hidden]
+        top, lg = tk.head_topk_bf16(h, w, k, logits=True)
+        torch.cuda.synchronize()
+        lgb = lg.view(torch.int16).cpu().numpy().view(np.uint16)
+        ok, msg = check_head_logits(lgb, hb[:, :hidden], wb[:, :hidden])
+        assert ok, f"{what}: {msg}"
+        assert_same(to_numpy(top), oracle.topk_bf16(lgb, vocab, k), what)
+
+
+def test_mismatched_out_is_rejected_before_launch():
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    hb, wb = head_inputs(4, 64, 300, seed=3)
+    h, w = _dev(hb), _dev(wb)
+    small = tk.head_topk_bf16(h, w, 8)
+    with pytest.raises(ValueError):
+        tk.head_topk_bf16(h, w, 16, out=small)
+    x = torch.zeros((4, 1000), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        tk.topk_bf16(x, 16, out=small)
+    with pytest.raises(ValueError):
+        tk.topk_f32(x.float(), 8, out=small)  # bf16 values for 4-byte entries

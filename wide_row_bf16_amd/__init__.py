@@ -172,6 +172,40 @@ def _current_stream_handle(torch, dev: int) -> int:
     return int(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _dtypes(torch, fmt: str):
+    """Accepted dtypes of an entry-value tensor for an input format."""
+    if fmt == "f32":
+        return (torch.float32, torch.int32, torch.uint32)
+    if fmt == "f16":
+        return (torch.float16, torch.int16, torch.uint16)
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _check_tensor(t, name: str, dtypes, shape, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: expected dtype in {[str(d) for d in dtypes]}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+
+
+def _check_out(torch, out, rows: int, k: int, fmt: str, device):
+    """Caller-supplied outputs must be exactly what the kernels write: int32
+    [rows, k] indices, [rows, k] values of the format's width, int32 [rows]
+    counts and masks, contiguous, on the input's device.  Anything else would
+    let the kernels write past the tensors, so it is rejected before any call."""
+    if not isinstance(out, tuple) or len(out) != 4:
+        raise ValueError("out: expected a TopK (idx, val, count, nonfinite)")
+    i32 = (torch.int32,)
+    _check_tensor(out[0], "out.idx", i32, (rows, k), device)
+    _check_tensor(out[1], "out.val", _dtypes(torch, fmt), (rows, k), device)
+    _check_tensor(out[2], "out.count", i32, (rows,), device)
+    _check_tensor(out[3], "out.nonfinite", (torch.int32, torch.uint32), (rows,), device)
+
+
 def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool = False, general: bool = False,
               out: TopK | None = None, stream=None, _fmt: str = "bf16") -> TopK:
     """Row-wise exact top-k of a 2-D bf16 tensor (see the module docstring).
@@ -208,6 +242,8 @@ def topk_bf16(x, k: int, *, cols: int | None = None, spans: int = 0, exact: bool
             torch.empty((rows,), dtype=torch.int32, device=x.device),
             torch.empty((rows,), dtype=torch.int32, device=x.device),
         )
+    else:
+        _check_out(torch, out, rows, k, _fmt, x.device)
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
     args = (rows, cols, row_stride, k, x.data_ptr(), out.idx.data_ptr(), out.val.data_ptr(), out.count.data_ptr(),
@@ -256,7 +292,10 @@ def topk_bf16_shard(x, k: int, col_base: int, *, out: TopK | None = None) -> Top
     rows, cols = x.shape
     if rows > 0 and cols > 0 and x.stride(1) != 1:
         raise ValueError("the last dimension must be contiguous")
-    out = _outputs(torch, rows, k, x.device) if out is None else out
+    if out is None:
+        out = _outputs(torch, rows, k, x.device)
+    else:
+        _check_out(torch, out, rows, k, "bf16", x.device)
     status = int(load().tk_topk_bf16_shard(
         rows, cols, x.stride(0) if rows > 1 else max(cols, 1), k, col_base, x.data_ptr(), out.idx.data_ptr(),
         out.val.data_ptr(), out.count.data_ptr(), out.nonfinite.data_ptr(),
@@ -271,14 +310,19 @@ def merge_topk_bf16(idx, val, count, nonfinite, *, out: TopK | None = None) -> T
     [shards, rows], all contiguous (tk_merge_topk_bf16)."""
     import torch
 
+    if idx.dim() != 3:
+        raise ValueError("idx: expected [shards, rows, k]")
     shards, rows, k = idx.shape
-    for t in (idx, val, count, nonfinite):
-        if not t.is_contiguous() or t.device.type != "cuda":
-            raise ValueError("expected contiguous tensors on a HIP device")
-    if tuple(val.shape) != (shards, rows, k) or tuple(count.shape) != (shards, rows) or \
-            tuple(nonfinite.shape) != (shards, rows):
-        raise ValueError("shape mismatch between the stacked shard results")
-    out = _outputs(torch, rows, k, idx.device) if out is None else out
+    if idx.device.type != "cuda":
+        raise ValueError("expected tensors on a HIP device")
+    _check_tensor(idx, "idx", (torch.int32,), (shards, rows, k), idx.device)
+    _check_tensor(val, "val", _dtypes(torch, "bf16"), (shards, rows, k), idx.device)
+    _check_tensor(count, "count", (torch.int32,), (shards, rows), idx.device)
+    _check_tensor(nonfinite, "nonfinite", (torch.int32, torch.uint32), (shards, rows), idx.device)
+    if out is None:
+        out = _outputs(torch, rows, k, idx.device)
+    else:
+        _check_out(torch, out, rows, k, "bf16", idx.device)
     status = int(load().tk_merge_topk_bf16(
         rows, shards, k, idx.data_ptr(), val.data_ptr(), count.data_ptr(), nonfinite.data_ptr(), out.idx.data_ptr(),
         out.val.data_ptr(), out.count.data_ptr(), out.nonfinite.data_ptr(),
@@ -299,13 +343,18 @@ def sample_topk_bf16(topk: TopK, temperature: float, top_p: float, seed: int, of
     returns (token, kept), int32 [rows] each."""
     import torch
 
+    if topk.idx.dim() != 2 or topk.idx.device.type != "cuda":
+        raise ValueError("expected a TopK of [rows, k] tensors on a HIP device")
     rows, k = topk.idx.shape
-    for t in topk:
-        if not t.is_contiguous() or t.device.type != "cuda":
-            raise ValueError("expected contiguous tensors on a HIP device")
+    _check_out(torch, topk, rows, k, "bf16", topk.idx.device)
     if out is None:
         out = (torch.empty((rows,), dtype=torch.int32, device=topk.idx.device),
                torch.empty((rows,), dtype=torch.int32, device=topk.idx.device))
+    else:
+        if len(out) != 2:
+            raise ValueError("out: expected (token, kept)")
+        _check_tensor(out[0], "out token", (torch.int32,), (rows,), topk.idx.device)
+        _check_tensor(out[1], "out kept", (torch.int32,), (rows,), topk.idx.device)
     dev = topk.idx.device.index if topk.idx.device.index is not None else torch.cuda.current_device()
     status = int(load().tk_sample_topk_bf16(
         rows, k, topk.idx.data_ptr(), topk.val.data_ptr(), topk.count.data_ptr(), float(temperature), float(top_p),
@@ -336,11 +385,15 @@ def head_topk_bf16(h, w, k: int, *, logits: bool = False, out: TopK | None = Non
             raise ValueError("the last dimension must be contiguous")
     rows, hidden = h.shape
     vocab = w.shape[0]
+    if w.device != h.device:
+        raise ValueError("h and w must be on the same device")
     if out is None:
         out = TopK(torch.empty((rows, k), dtype=torch.int32, device=h.device),
                    torch.empty((rows, k), dtype=torch.bfloat16, device=h.device),
                    torch.empty((rows,), dtype=torch.int32, device=h.device),
                    torch.empty((rows,), dtype=torch.int32, device=h.device))
+    else:
+        _check_out(torch, out, rows, k, "bf16", h.device)
     lg = torch.empty((rows, vocab), dtype=torch.bfloat16, device=h.device) if logits else None
     dev = h.device.index if h.device.index is not None else torch.cuda.current_device()
     status = int(load().tk_head_topk_bf16(

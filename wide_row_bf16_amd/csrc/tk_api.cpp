@@ -120,7 +120,9 @@ tk_status guard_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, con
   if (vocab < 1 || vocab > INT32_MAX) return TK_ERR_SHAPE;
   if (h_stride < hidden || w_stride < hidden || h_stride % 8 != 0 || w_stride % 8 != 0) return TK_ERR_SHAPE;
   if (h_stride > kHeadMaxStride || w_stride > kHeadMaxStride) return TK_ERR_SHAPE;
-  if (logits && logits_stride < vocab) return TK_ERR_SHAPE;
+  // logits rows are addressed as r * logits_stride + column in 64 bits
+  if (logits && (logits_stride < vocab || logits_stride > (std::numeric_limits<int64_t>::max() / 8 - vocab) / 64))
+    return TK_ERR_SHAPE;
   if (k < 1 || k > kMaxK) return TK_ERR_K;
   if (rows == 0) return TK_OK;
   if (!h || !w || !out_idx || !out_val || !out_count || !out_nonfinite) return TK_ERR_NULL;

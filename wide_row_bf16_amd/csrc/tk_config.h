@@ -1,7 +1,10 @@
 // Compile-time constants of the top-k library, shared by its kernels and its
-// host code.  Tying them together here (with static_asserts) means a change to
-// one of them fails the build instead of a merge -- the same protection the
-// TensorFold PR #713 change 3 describes for its lane, span and max_k constants.
+// host code.  The static_asserts at the end check that the kernels' limits
+// equal the public header's (TK_MAX_K, TK_MAX_K_LANE, TK_HEAD_MAX_ROWS), that
+// a wave can hold one kept entry per lane, and that every column a wave scans
+// fits its 16-bit relative index; an edit to one constant that breaks any of
+// these relations stops compilation.  (Cited: TensorFold PR #713, change 3,
+// which checks its kernel constants against the calling side at build time.)
 #pragma once
 
 #include <stdint.h>

@@ -111,10 +111,15 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   const int l = lane_id();
   const int64_t nvalid = a.vocab - n0 < kHeadSpanCols ? a.vocab - n0 : kHeadSpanCols;
 
+  // Both ranges end at the last row's `hidden`-th element, never in its row
+  // padding: the loads below read whole blocks past `hidden`, which the
+  // range check turns into zeros on the last row (and which are zeroed in
+  // registers on the others).  Ranges and offsets are multiples of 16 bytes
+  // (hidden % 32 == 0, strides % 8 == 0), so no load straddles the end.
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.w + n0 * a.w_stride), (short)0, (int)(nvalid * a.w_stride * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rh =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.h, (short)0, (int)(a.rows * a.h_stride * 2), kBufferWord3);
+      (void *)(a.w + n0 * a.w_stride), (short)0, (int)(((nvalid - 1) * a.w_stride + a.hidden) * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.h, (short)0, (int)(((a.rows - 1) * a.h_stride + a.hidden) * 2), kBufferWord3);
 
   f32x4 acc[kHeadTilesPerWave][RT];
 #pragma unroll
