@@ -311,6 +311,25 @@ tk_status tk_validate_head_bf16(int64_t rows, int64_t hidden, int64_t vocab, int
                                 const uint16_t *logits, int64_t logits_stride);
 
 /*
+ * Measurement probe, beside the top-k rather than part of it.  TensorFold PR
+ * #713, change 3 measures its span path against a control dispatch in a
+ * bench of its own; here the control of a scan's time is the bare read of
+ * the same bytes: `bytes` (a multiple of 16) of device memory at `in`
+ * (16-byte aligned) are streamed by `workgroups` workgroups of four waves
+ * with exactly the loads of the top-k scan (four nontemporal 16-byte vectors
+ * per lane per chunk, two chunks in flight) and nothing is computed from
+ * them.  `sink` (device, uint32 [8192], 4-byte aligned) is written only if
+ * the bytes' XOR fold hits a fixed sentinel (it keeps the loads from being
+ * dropped).  bytes == 0 launches an empty kernel of `workgroups` workgroups
+ * (in may be NULL): the launch floor of that grid.
+ * Errors: TK_ERR_SHAPE (bytes < 0 or not a multiple of 16, workgroups < 1
+ * or > 2^24, a wave's share of 2^26 vectors or more), TK_ERR_NULL,
+ * TK_ERR_ALIGN, TK_ERR_ALIAS (sink inside the read range), TK_ERR_DEVICE.
+ * Asynchronous on `stream`; no scratch memory.
+ */
+tk_status tk_probe_read(const void *in, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
+
+/*
  * tk_max_k: TK_MAX_K, the largest k of the row top-k as built.  TensorFold PR
  * #713, change 3 ties the kernel's lane, span and max_k constants to the
  * calling side at compile time, so that a mismatch breaks the build; here the

@@ -329,3 +329,19 @@ def test_binding_rejects_mismatched_out_tensors():
     with pytest.raises(ValueError):  # outputs on another device than the input
         tk._check_out(torch, _cpu_out(torch, 4, 8), 4, 8, "bf16", torch.device("cuda", 0))
 
+
+
+def test_probe_read_guards():
+    """The measurement probe rejects bad arguments before any launch."""
+    lib = tk.load()
+    S = 0x70000000
+    assert lib.tk_probe_read(IN, -16, 4, S, None) == SHAPE
+    assert lib.tk_probe_read(IN, 17, 4, S, None) == SHAPE
+    assert lib.tk_probe_read(IN, 1024, 0, S, None) == SHAPE
+    assert lib.tk_probe_read(IN, 1024, 2**24 + 1, S, None) == SHAPE
+    assert lib.tk_probe_read(IN, 16 * 4 * 2**26, 1, S, None) == SHAPE   # a wave's share too large
+    assert lib.tk_probe_read(None, 1024, 4, S, None) == NULL
+    assert lib.tk_probe_read(IN, 1024, 4, None, None) == NULL
+    assert lib.tk_probe_read(IN + 8, 1024, 4, S, None) == ALIGN
+    assert lib.tk_probe_read(IN, 1024, 4, S + 2, None) == ALIGN
+    assert lib.tk_probe_read(IN, 1 << 20, 4, IN + 4096, None) == ALIAS

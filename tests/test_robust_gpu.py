@@ -103,9 +103,16 @@ def test_rejected_calls_write_nothing():
         with pytest.raises(tk.TkError) as e:
             tk.topk_bf16(x, 8, out=out, **kw)
         assert e.value.status == 7
+    for b in bufs:
+        assert np.all(b.cpu().numpy() == CANARY)
+    bufs, out = canaried_outputs(4, 257)  # outputs of the right shape: the library's own k guard rejects
     with pytest.raises(tk.TkError) as e:
         tk.topk_bf16(x, 257, out=out)
     assert e.value.status == 3
+    for b in bufs:
+        assert np.all(b.cpu().numpy() == CANARY)
+    with pytest.raises(ValueError):  # outputs of another k: the binding rejects before any call
+        tk.topk_bf16(x, 16, out=out)
     for b in bufs:
         assert np.all(b.cpu().numpy() == CANARY)
 
@@ -176,3 +183,22 @@ def test_library_loaded_before_torch():
     want = oracle.topk_bf16(m, 5000, 16)
     assert np.array_equal(np.array(idx, dtype=np.int32), want[0])
     assert np.array_equal(np.array(count, dtype=np.int32), want[2])
+
+
+def test_read_probe_reads_and_writes_nothing():
+    """The measurement probe streams a buffer (and, with no buffer, launches an
+    empty grid) without writing anything: its sink keeps its contents."""
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    sink = torch.full((8192,), 7, dtype=torch.int32, device="cuda")
+    for n, wgs in ((1 << 20, 64), (4096 * 16 + 48, 300), (16, 1)):
+        x = torch.zeros((n // 2,), dtype=torch.int16, device="cuda")
+        tk.read_probe(x, wgs, sink)
+    tk.read_probe(None, 180, sink)
+    torch.cuda.synchronize()
+    assert np.all(sink.cpu().numpy() == 7)
+    with pytest.raises(tk.TkError) as e:
+        tk.read_probe(torch.zeros((9,), dtype=torch.int16, device="cuda"), 4, sink)  # 18 bytes
+    assert e.value.status == 2

@@ -37,6 +37,7 @@ EXPORTS = (
     "tk_validate_f32", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
     "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_head_topk_bf16",
     "tk_validate_head_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
+    "tk_probe_read",
 )
 
 
@@ -123,6 +124,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_status_string.argtypes = [i32]
     lib.tk_build_info.restype = ctypes.c_char_p
     lib.tk_build_info.argtypes = []
+    lib.tk_probe_read.restype = i32
+    lib.tk_probe_read.argtypes = [vp, i64, i32, vp, vp]
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -417,3 +420,22 @@ def validate_sample(rows, k, idx_ptr, val_ptr, count_ptr, temperature, top_p, to
     """The host-side guards of tk_sample_topk_bf16 on raw pointers (no HIP call)."""
     return int(load().tk_validate_sample_bf16(rows, k, idx_ptr, val_ptr, count_ptr, temperature, top_p, token_ptr,
                                               kept_ptr))
+
+
+def read_probe(x, workgroups: int, sink) -> None:
+    """Measurement probe (tk_probe_read): streams the bytes of the contiguous
+    device tensor ``x`` with the scan's loads over ``workgroups`` workgroups
+    and computes nothing; ``x=None`` launches an empty kernel.  ``sink`` is a
+    device int32 tensor of 8192 elements."""
+    import torch
+
+    if sink.numel() < 8192 or sink.element_size() != 4 or not sink.is_contiguous():
+        raise ValueError("sink: expected 8192 contiguous 4-byte elements")
+    if x is not None and not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    nbytes = 0 if x is None else x.numel() * x.element_size()
+    dev = sink.device.index if sink.device.index is not None else torch.cuda.current_device()
+    status = int(load().tk_probe_read(None if x is None else x.data_ptr(), nbytes, workgroups, sink.data_ptr(),
+                                      _current_stream_handle(torch, dev)))
+    if status != TK_OK:
+        raise TkError(status, "tk_probe_read")

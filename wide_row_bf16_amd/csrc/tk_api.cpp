@@ -1049,6 +1049,18 @@ int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_uni
   return plan(rows, cols, cus);
 }
 
+tk_status tk_probe_read(const void *in, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream) {
+  if (bytes < 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > kMaxBlocksPerLaunch) return TK_ERR_SHAPE;
+  // each wave's share must fit the loads' 32-bit descriptor range
+  if (bytes / 16 / ((int64_t)workgroups * tk::kWgWaves) + 1 > (int64_t(1) << 26)) return TK_ERR_SHAPE;
+  if ((bytes > 0 && !in) || !sink) return TK_ERR_NULL;
+  if (((uintptr_t)in & 15) || ((uintptr_t)sink & 3)) return TK_ERR_ALIGN;
+  const Range rin{(uintptr_t)in, (uintptr_t)in + (uintptr_t)bytes}, rsink{(uintptr_t)sink, (uintptr_t)sink + 4 * 8192};
+  if (overlap(rin, rsink)) return TK_ERR_ALIAS;
+  return tk::launch_read_probe(in, bytes / 16, workgroups, sink, (hipStream_t)stream) == hipSuccess ? TK_OK
+                                                                                                    : TK_ERR_DEVICE;
+}
+
 int32_t tk_max_k(void) { return kMaxKWide; }
 
 int64_t tk_max_span_cols(void) { return tk::kMaxSpanCols; }

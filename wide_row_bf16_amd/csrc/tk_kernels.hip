@@ -945,6 +945,47 @@ hipError_t launch_shard_merge(const ShardMergeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Measurement probe (not part of the top-k): streams nvec 16-byte vectors,
+// split evenly over the grid's workgroups and each workgroup's four waves,
+// with the scan's loads -- chunks of four nontemporal vectors per lane, two
+// chunks in flight, range-checked descriptors -- and folds them with XOR.
+// Nothing is written unless the fold hits a sentinel, so the loads cannot be
+// dropped; with nvec = 0 the kernel is empty.  Its time is the floor any scan
+// of those bytes with that grid can reach.
+__global__ __launch_bounds__(kWgThreads) void read_probe_kernel(const uint4 *in, int64_t nvec, uint32_t *sink) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t g = gridDim.x, b = blockIdx.x;
+  const int64_t j0 = nvec * b / g, j1 = nvec * (b + 1) / g;
+  const int64_t w0 = j0 + (j1 - j0) * wave / kWgWaves, w1 = j0 + (j1 - j0) * (wave + 1) / kWgWaves;
+  const uint32_t wn = (uint32_t)(w1 - w0);
+  uint32_t acc = 0;
+  auto fold = [&](const uint4 (&v)[kChunkVecs]) {
+#pragma unroll
+    for (int u = 0; u < kChunkVecs; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  };
+  if (wn > 0) {
+    const uint4 *vp = in + w0;
+    const uint32_t lane_off = (uint32_t)lane_id() * 16u;
+    uint4 A[kChunkVecs], B[kChunkVecs];
+    load_chunk(A, vp, wn, 0, lane_off);
+    for (uint32_t first = 0; first < wn; first += 2 * kStep) {
+      load_chunk(B, vp, wn, first + kStep, lane_off);
+      fold(A);
+      if (first + kStep >= wn) break;
+      load_chunk(A, vp, wn, first + 2 * kStep, lane_off);
+      fold(B);
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[b & 8191] = acc;
+}
+
+hipError_t launch_read_probe(const void *in, int64_t nvec, int32_t workgroups, uint32_t *sink, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3((uint32_t)workgroups), dim3(kWgThreads), 0, stream,
+                     (const uint4 *)in, nvec, sink);
+  return hipGetLastError();
+}
+
 __global__ void zero_fill_kernel(int32_t *p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;

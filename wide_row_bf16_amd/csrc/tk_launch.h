@@ -200,5 +200,8 @@ hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStr
 hipError_t launch_wide_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
+// Measurement probe: nvec 16-byte vectors read with the scan's loads over
+// `workgroups` workgroups of four waves (nvec = 0: an empty kernel).
+hipError_t launch_read_probe(const void *in, int64_t nvec, int32_t workgroups, uint32_t *sink, hipStream_t stream);
 
 }  // namespace tk
