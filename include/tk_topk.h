@@ -75,7 +75,8 @@ typedef enum tk_status {
   TK_ERR_ALIGN = 4,  /* in/out_val not 2-byte aligned, or out_idx/out_count/out_nonfinite not 4-byte aligned */
   TK_ERR_ALIAS = 5,  /* two of the five buffers overlap (outputs must not alias the input or each other) */
   TK_ERR_DEVICE = 6, /* HIP reported an error while allocating or launching */
-  TK_ERR_OPTION = 7  /* tk_options out of range */
+  TK_ERR_OPTION = 7, /* tk_options out of range */
+  TK_ERR_SCRATCH = 8 /* tk_topk_bf16_noalloc: one row needs more scratch than its fixed array holds */
 } tk_status;
 
 /*
@@ -92,6 +93,29 @@ typedef enum tk_status {
 tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
                        int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                        void *stream);
+
+/*
+ * tk_topk_bf16 without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments, results, guards and errors as
+ * tk_topk_bf16; the scratch it needs (the span lists and arrival counters of
+ * split rows) lives in one fixed device array per GPU of
+ * TK_NOALLOC_SCRATCH_BYTES, set up on the first call on that GPU (with it
+ * current) and held until the process ends.  No hipMalloc, hipFree or
+ * allocating library call is made, ever.  Split rows are processed in row
+ * batches small enough for the array; a call whose single row needs more
+ * scratch than the array holds (only rows of over a billion columns) returns
+ * TK_ERR_SCRATCH before any launch.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams, or
+ * from different threads) race and must be ordered by the caller; calls on
+ * one stream are ordered by the stream.  The array's arrival counters are
+ * zero before and after every call.
+ */
+#define TK_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+tk_status tk_topk_bf16_noalloc(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                               int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                               void *stream);
 
 /*
  * Planning overrides, for tests and benchmarks.  The result never depends on

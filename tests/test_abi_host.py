@@ -39,7 +39,7 @@ def test_constants():
     assert int(re.search(r"#define TK_MAX_K_LANE (\d+)u", text).group(1)) == 64
     assert tk.max_span_cols() >= 4 * 65000
     assert b"gfx950" in tk.load().tk_build_info()
-    for s in range(8):
+    for s in range(9):
         assert tk.load().tk_status_string(s)
 
 

@@ -26,7 +26,7 @@ LIBRARY = os.path.join(PKG, "libtk_topk.so")
 TK_OK = 0
 STATUS_NAMES = {
     0: "TK_OK", 1: "TK_ERR_NULL", 2: "TK_ERR_SHAPE", 3: "TK_ERR_K", 4: "TK_ERR_ALIGN",
-    5: "TK_ERR_ALIAS", 6: "TK_ERR_DEVICE", 7: "TK_ERR_OPTION",
+    5: "TK_ERR_ALIAS", 6: "TK_ERR_DEVICE", 7: "TK_ERR_OPTION", 8: "TK_ERR_SCRATCH",
 }
 NONFINITE_NAN, NONFINITE_POSINF, NONFINITE_NEGINF = 1, 2, 4
 FILL_IDX, FILL_VAL = -1, 0x7FC0
@@ -37,7 +37,7 @@ EXPORTS = (
     "tk_validate_f32", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
     "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_head_topk_bf16",
     "tk_validate_head_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
-    "tk_probe_read",
+    "tk_probe_read", "tk_topk_bf16_noalloc",
 )
 
 
@@ -85,6 +85,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.tk_topk_bf16.restype = i32
     lib.tk_topk_bf16.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.tk_topk_bf16_noalloc.restype = i32
+    lib.tk_topk_bf16_noalloc.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.tk_topk_bf16_ex.restype = i32
     lib.tk_topk_bf16_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TkOptions)]
     lib.tk_topk_f16.restype = i32

@@ -314,6 +314,54 @@ tk_status acquire_scratch(int dev, hipStream_t stream, size_t total, char **base
   return TK_OK;
 }
 
+// Where a call's scratch comes from.  Cached: the (device, stream) buffer of
+// the allocating entry points, grown stream-ordered.  Fixed: the device's
+// fixed array (tk_topk_bf16_noalloc), never allocated or freed; row batches
+// shrink until their scratch fits it.
+struct Place {
+  int dev;
+  hipStream_t stream;
+  bool fixed;
+};
+
+// The largest batch of at most `want` rows whose scratch bytes(batch) fits
+// the place: `want` itself for the cached scratch; 0 when not even one row
+// fits the fixed array.
+template <class Bytes>
+int64_t fit_batch(const Place &p, int64_t want, Bytes bytes) {
+  if (!p.fixed || bytes(want) <= tk::kFixedScratchBytes) return want;
+  int64_t lo = 0, hi = want;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (bytes(mid) <= tk::kFixedScratchBytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// `total` bytes of scratch for one call at *base, with the arrival counters
+// zero at its start (see acquire_scratch).  *owned: the caller frees it,
+// stream-ordered, after its last launch (cached place only).  The caller
+// holds g_scratch_mu for the cached place.
+tk_status take_scratch(const Place &p, size_t total, char **base, bool *owned) {
+  *owned = false;
+  if (p.fixed) {
+    if (total > tk::kFixedScratchBytes) return TK_ERR_SCRATCH;
+    void *ptr = nullptr;
+    if (tk::fixed_scratch(p.dev, p.stream, &ptr) != hipSuccess) return TK_ERR_DEVICE;
+    *base = (char *)ptr;
+    return TK_OK;
+  }
+  keep_pool(p.dev);
+  return acquire_scratch(p.dev, p.stream, total, base, owned);
+}
+
+// Holds g_scratch_mu for the cached place only: calls through the fixed
+// array are documented to race when they overlap on one device.
+std::unique_lock<std::mutex> scratch_lock(const Place &p) {
+  return p.fixed ? std::unique_lock<std::mutex>() : std::unique_lock<std::mutex>(g_scratch_mu);
+}
+
 // k = 1: span plan of the argmax scan.  On few rows a call is latency bound:
 // each extra workgroup costs about 9 ns of dispatch, while a workgroup streams
 // its span with a fixed number of bytes in flight, so its time grows with the
@@ -351,8 +399,9 @@ int32_t plan_argmax(int64_t rows, int64_t cols, int32_t compute_units) {
 // 2 <= spans <= kMergeGroup writes one slot per (row, span) after the arrival
 // counters, in batches of at most kFusedMaxRows rows.
 tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t *in, int32_t *out_idx,
-                     uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, hipStream_t stream, int dev,
+                     uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, const Place &place,
                      int32_t spans, int64_t col_base, uint32_t inf) {
+  const hipStream_t stream = place.stream;
   tk::ArgmaxArgs a{};
   a.in = in;
   a.cols = cols;
@@ -374,14 +423,15 @@ tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t 
     return TK_OK;
   }
   const int64_t batch_cap = rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
-  const int64_t batch = rows < batch_cap ? rows : batch_cap;
   const size_t off_slot = align256((size_t)kFusedMaxRows * sizeof(int32_t));
-  const size_t total = align256(off_slot + (size_t)batch * (size_t)spans * sizeof(uint64_t));
-  keep_pool(dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto bytes = [&](int64_t b) { return align256(off_slot + (size_t)b * (size_t)spans * sizeof(uint64_t)); };
+  const int64_t batch = fit_batch(place, rows < batch_cap ? rows : batch_cap, bytes);
+  if (batch < 1) return TK_ERR_SCRATCH;
+  const size_t total = bytes(batch);
+  auto lock = scratch_lock(place);
   char *base = nullptr;
   bool owned = false;
-  const tk_status sst = acquire_scratch(dev, stream, total, &base, &owned);
+  const tk_status sst = take_scratch(place, total, &base, &owned);
   if (sst != TK_OK) return sst;
   tk_status result = TK_OK;
   for (int64_t r0 = 0; r0 < rows; r0 += batch) {
@@ -421,9 +471,10 @@ int32_t plan_wide(int64_t rows, int64_t cols, int32_t compute_units) {
 }
 
 tk_status run_wide(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
-                   uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, hipStream_t stream, int dev,
+                   uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, const Place &place,
                    int32_t forced, int32_t exact, int64_t col_base, uint32_t inf) {
-  const int32_t spans = forced > 0 ? forced : plan_wide(rows, cols, device_cus(dev));
+  const hipStream_t stream = place.stream;
+  const int32_t spans = forced > 0 ? forced : plan_wide(rows, cols, device_cus(place.dev));
   if (spans > kMergeGroup) return TK_ERR_SHAPE;  // excluded by the guards; kept as a bound on the fold
   tk::ScanArgs sa{};
   sa.in = in;
@@ -449,17 +500,21 @@ tk_status run_wide(int64_t rows, int64_t cols, int64_t stride, int32_t k, const 
     return TK_OK;
   }
   const int64_t batch_cap = rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
-  const int64_t batch = rows < batch_cap ? rows : batch_cap;
-  const size_t nlists = (size_t)batch * (size_t)spans;
-  const size_t off_list = align256((size_t)kFusedMaxRows * sizeof(int32_t));
-  const size_t off_count = align256(off_list + nlists * (size_t)k * sizeof(uint64_t));
-  const size_t off_flags = align256(off_count + nlists * sizeof(int32_t));
-  const size_t total = align256(off_flags + nlists * sizeof(uint32_t));
-  keep_pool(dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  size_t off_list = 0, off_count = 0, off_flags = 0;
+  auto bytes = [&](int64_t b) {
+    const size_t nlists = (size_t)b * (size_t)spans;
+    off_list = align256((size_t)kFusedMaxRows * sizeof(int32_t));
+    off_count = align256(off_list + nlists * (size_t)k * sizeof(uint64_t));
+    off_flags = align256(off_count + nlists * sizeof(int32_t));
+    return align256(off_flags + nlists * sizeof(uint32_t));
+  };
+  const int64_t batch = fit_batch(place, rows < batch_cap ? rows : batch_cap, bytes);
+  if (batch < 1) return TK_ERR_SCRATCH;
+  const size_t total = bytes(batch);  // also sets the offsets for this batch
+  auto lock = scratch_lock(place);
   char *base = nullptr;
   bool owned = false;
-  const tk_status sst = acquire_scratch(dev, stream, total, &base, &owned);
+  const tk_status sst = take_scratch(place, total, &base, &owned);
   if (sst != TK_OK) return sst;
   tk_status result = TK_OK;
   for (int64_t r0 = 0; r0 < rows; r0 += batch) {
@@ -513,11 +568,11 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
     total = align256(total + nlists * sizeof(uint32_t));
   }
   const size_t off0 = align256((size_t)kFusedMaxRows * sizeof(int32_t));  // the counters stay untouched
-  keep_pool(dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  const Place place{dev, stream, false};
+  auto lock = scratch_lock(place);
   char *base = nullptr;
   bool owned = false;
-  const tk_status sst = acquire_scratch(dev, stream, off0 + total, &base, &owned);
+  const tk_status sst = take_scratch(place, off0 + total, &base, &owned);
   if (sst != TK_OK) return sst;
   base += off0;
   tk_status result = TK_OK;
@@ -570,7 +625,7 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
 
 tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint16_t *in, int32_t *out_idx,
               uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite, void *stream_handle,
-              const tk_options *opt, int64_t col_base = 0, uint32_t inf = 0x7F80u) {
+              const tk_options *opt, int64_t col_base = 0, uint32_t inf = 0x7F80u, bool fixed = false) {
   tk_status st = guard(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite);
   if (st != TK_OK) return st;
   if (col_base < 0 || col_base > (int64_t)INT32_MAX - cols + (cols > 0 ? 1 : 0)) return TK_ERR_SHAPE;
@@ -593,8 +648,9 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   hipStream_t stream = (hipStream_t)stream_handle;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  const Place place{dev, stream, fixed};
   if (k > kMaxK)
-    return run_wide(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, dev, forced,
+    return run_wide(rows, cols, stride, k, in, out_idx, out_val, out_count, out_nonfinite, place, forced,
                     exact, col_base, inf);
   // k = 1: the argmax scan on few rows (or a forced split); with a row for
   // every CU the general scan measured ~2% faster (49.0 vs 50.2 us on 1024 x
@@ -603,7 +659,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   if (k == 1 && !general && (forced > 0 || rows < device_cus(dev))) {
     const int32_t s1 = forced > 0 ? forced : plan_argmax(rows, cols, device_cus(dev));
     if (s1 <= kMergeGroup)
-      return run_argmax(rows, cols, stride, in, out_idx, out_val, out_count, out_nonfinite, stream, dev, s1,
+      return run_argmax(rows, cols, stride, in, out_idx, out_val, out_count, out_nonfinite, place, s1,
                         col_base, inf);
   }
   const int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
@@ -640,36 +696,34 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
   // the span lists itself (one dispatch); otherwise merge dispatches follow.
   const bool fused = spans <= kMergeGroup && rows_per_launch >= 1;
   const int64_t batch_cap = fused && rows_per_launch > kFusedMaxRows ? kFusedMaxRows : rows_per_launch;
-  const int64_t batch = rows < batch_cap ? rows : batch_cap;
   int32_t level_lists[8];
   int levels = 0;
   for (int32_t n = spans; n > 1; n = (n + kMergeGroup - 1) / kMergeGroup) level_lists[levels++] = n;
   if (fused) levels = 1;  // only the span lists
   const size_t counters_bytes = align256((size_t)kFusedMaxRows * sizeof(int32_t));
-  size_t off_list[8], off_count[8], off_flags[8], total = counters_bytes;
-  for (int i = 0; i < levels; ++i) {
-    const size_t nlists = (size_t)batch * (size_t)level_lists[i];
-    off_list[i] = total;
-    total = align256(total + nlists * (size_t)k * sizeof(uint64_t));
-    off_count[i] = total;
-    total = align256(total + nlists * sizeof(int32_t));
-    off_flags[i] = total;
-    total = align256(total + nlists * sizeof(uint32_t));
-  }
-  keep_pool(dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  tk_status sst = TK_OK;
-  bool fresh = false;
-  void *scratch = cached_scratch(dev, stream, total, &sst, &fresh);
+  size_t off_list[8], off_count[8], off_flags[8];
+  auto bytes = [&](int64_t b) {
+    size_t total = counters_bytes;
+    for (int i = 0; i < levels; ++i) {
+      const size_t nlists = (size_t)b * (size_t)level_lists[i];
+      off_list[i] = total;
+      total = align256(total + nlists * (size_t)k * sizeof(uint64_t));
+      off_count[i] = total;
+      total = align256(total + nlists * sizeof(int32_t));
+      off_flags[i] = total;
+      total = align256(total + nlists * sizeof(uint32_t));
+    }
+    return total;
+  };
+  const int64_t batch = fit_batch(place, rows < batch_cap ? rows : batch_cap, bytes);
+  if (batch < 1) return TK_ERR_SCRATCH;
+  const size_t total = bytes(batch);  // also sets the offsets for this batch
+  auto lock = scratch_lock(place);
+  char *base = nullptr;
+  bool owned = false;
+  const tk_status sst = take_scratch(place, total, &base, &owned);
   if (sst != TK_OK) return sst;
-  const bool owned = scratch == nullptr;
-  if (owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
-  char *base = (char *)scratch;
   int32_t *counters = (int32_t *)base;
-  if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
-    if (owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
-    return TK_ERR_DEVICE;
-  }
 
   tk_status result = TK_OK;
   for (int64_t r0 = 0; r0 < rows && result == TK_OK; r0 += batch) {
@@ -722,7 +776,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
       }
     }
   }
-  if (owned && hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  if (owned && hipFreeAsync(base, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
   return result;
 }
 
@@ -908,6 +962,13 @@ tk_status tk_topk_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32_t k
   return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr);
 }
 
+tk_status tk_topk_bf16_noalloc(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
+                               int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
+                               void *stream) {
+  return run(rows, cols, row_stride, k, in, out_idx, out_val, out_count, out_nonfinite, stream, nullptr, 0, 0x7F80u,
+             true);
+}
+
 tk_status tk_topk_bf16_ex(int64_t rows, int64_t cols, int64_t row_stride, int32_t k, const uint16_t *in,
                           int32_t *out_idx, uint16_t *out_val, int32_t *out_count, uint32_t *out_nonfinite,
                           void *stream, const tk_options *opt) {
@@ -1075,6 +1136,7 @@ const char *tk_status_string(tk_status s) {
     case TK_ERR_ALIAS: return "buffers overlap";
     case TK_ERR_DEVICE: return "HIP error while allocating or launching";
     case TK_ERR_OPTION: return "invalid tk_options";
+    case TK_ERR_SCRATCH: return "one row needs more scratch than the fixed array of tk_topk_bf16_noalloc holds";
   }
   return "unknown status";
 }

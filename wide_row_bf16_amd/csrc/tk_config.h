@@ -7,6 +7,7 @@
 // which checks its kernel constants against the calling side at build time.)
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "tk_topk.h"
@@ -32,6 +33,8 @@ constexpr int kSampleElems = kWgWaves * kChunkVecs * kWave * kVecElems;  // pool
 constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
 constexpr int kHeadSpanCols = 256;             // vocabulary columns per workgroup of the fused head
 constexpr int kHeadMaxRows = 64;               // rows of the fused head: four 16-row matrix-core tiles
+constexpr size_t kFixedScratchBytes = size_t(2) << 20;  // scratch array of the allocation-free entry point
+constexpr int kMaxDevices = 64;                // devices the library keeps per-device state for
 
 static_assert(kMaxKWide == (int)TK_MAX_K, "public and internal max k differ");
 static_assert(kMaxK == (int)TK_MAX_K_LANE, "public and internal lane max k differ");
@@ -44,5 +47,7 @@ static_assert(kWgThreads == 256, "scan kernels are written for four wave64s");
 static_assert(((kMaxSpanVecs + kWgWaves - 1) / kWgWaves) * kVecElems + 2 * kVecElems <= kMaxWaveCols,
               "a wave's column range must fit the 16-bit relative index");
 static_assert(kSampleElems == kWgWaves * kChunkVecs * kWave * kVecElems, "sample = one chunk per wave");
+static_assert(kFixedScratchBytes == (size_t)TK_NOALLOC_SCRATCH_BYTES, "public and internal fixed scratch differ");
+static_assert(kFixedScratchBytes >= 2 * (size_t)kFusedMaxRows * 4, "the fixed scratch holds the arrival counters");
 
 }  // namespace tk

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tk_config.h"
 #include "tk_launch.h"
 
@@ -995,6 +997,39 @@ hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(zero_fill_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
+}
+
+// The fixed scratch of tk_topk_bf16_noalloc: one array per device, held
+// until the process ends, for callers that cannot allocate.  Its first
+// kFusedMaxRows int32 are the fused folds' arrival counters, which every
+// call leaves at zero.  In host code `scratch` names a host-side stand-in,
+// never device memory: kernels and fills get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kFixedScratchBytes];
+
+namespace {
+std::mutex g_fixed_mu;
+void *g_fixed_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t fixed_scratch(int dev, hipStream_t stream, void **ptr) {
+  *ptr = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_fixed_mu);
+  if (!g_fixed_ptr[dev]) {
+    // the caller has made `dev` current: this is that device's copy
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // device globals start zeroed; the fill makes the counters' zero state
+    // explicit, ordered before this call's kernels on the caller's stream
+    const hipError_t f = launch_zero_fill((int32_t *)p, kFusedMaxRows, stream);
+    if (f != hipSuccess) return f;
+    g_fixed_ptr[dev] = p;
+  }
+  *ptr = g_fixed_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_span_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream_t stream) {

@@ -200,6 +200,11 @@ hipError_t launch_argmax32(const ArgmaxArgs32 &a, int64_t rows_in_launch, hipStr
 hipError_t launch_wide_scan32(const ScanArgs32 &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream);
 hipError_t launch_zero_fill(int32_t *p, int64_t n, hipStream_t stream);
+// Device address of the current device's fixed scratch array
+// (kFixedScratchBytes, 256-byte aligned; its first kFusedMaxRows int32 are
+// zero between calls), set up on the first request for `dev`, which must be
+// the current device.
+hipError_t fixed_scratch(int dev, hipStream_t stream, void **ptr);
 // Measurement probe: nvec 16-byte vectors read with the scan's loads over
 // `workgroups` workgroups of four waves (nvec = 0: an empty kernel).
 hipError_t launch_read_probe(const void *in, int64_t nvec, int32_t workgroups, uint32_t *sink, hipStream_t stream);
