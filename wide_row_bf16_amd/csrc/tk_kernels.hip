@@ -346,13 +346,24 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
     s_fl[wave] = fl;
   }
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int o = 1; o < kWgWaves; ++o) {
-      acc = merge_sorted64(acc, s_acc[o][l], x);
-      cnt += s_cnt[o];
-      fl |= s_fl[o];
+  // the waves' results as a tree: 0 and 2 take 1 and 3, then 0 takes 2
+  if ((wave & 1) == 0) {
+    acc = merge_sorted64(acc, s_acc[wave + 1][l], x);
+    cnt += s_cnt[wave + 1];
+    fl |= s_fl[wave + 1];
+  }
+  if (wave == 2) {
+    s_acc[2][l] = acc;
+    if (l == 0) {
+      s_cnt[2] = cnt;
+      s_fl[2] = fl;
     }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    acc = merge_sorted64(acc, s_acc[2][l], x);
+    cnt += s_cnt[2];
+    fl |= s_fl[2];
     const int k = a.k;
     if (cnt > k) cnt = k;
     const int64_t ob = r * k;
@@ -502,40 +513,41 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   }
   if (total > a.k) total = a.k;
 
-  const uint64_t x = s_list[wave][l];
-  const bool mine = l < s_count[wave];
-  int rank = l;
-  if (mine) {
-#pragma unroll
-    for (int o = 0; o < kWgWaves; ++o)
-      if (o != wave) rank += count_beating(s_list[o], s_count[o], x);
+  // The four wave lists meet as a tree in registers: waves 0 and 2 merge
+  // their list with the next wave's, then wave 0 merges in wave 2's result.
+  // A wave's entries past its count (beaten by k of its own, or empty
+  // zeros) can only land at merged ranks >= k, so whole lists are merged.
+  const Xchg xm = make_xchg();
+  uint64_t acc = s_list[wave][l];
+  if ((wave & 1) == 0) acc = merge_sorted64(acc, s_list[wave + 1][l], xm);
+  if (wave == 2) s_list[2][l] = acc;  // wave 0 does not read its own slot's partner until after the barrier
+  __syncthreads();
+  if (wave == 0) {
+    acc = merge_sorted64(acc, s_list[2][l], xm);
+    if (S == 1) {
+      const int64_t ob = r * a.k;
+      if (l < total) {
+        a.out_idx[ob + l] = (int32_t)(col_of(acc) + a.col_base);
+        a.out_val[ob + l] = value_bits(acc, row);
+      } else if (l < a.k) {
+        a.out_idx[ob + l] = TK_FILL_IDX;
+        a.out_val[ob + l] = (uint16_t)TK_FILL_VAL;
+      }
+      if (l == 0) {
+        a.out_count[r] = total;
+        a.out_nonfinite[r] = flags;
+      }
+    } else {
+      // agent-scope stores: coherent across the XCDs' caches (see fold_row_if_last)
+      const int64_t sb = r * S + s;
+      if (l < total) __hip_atomic_store(&a.span_list[sb * a.k + l], acc, __ATOMIC_RELAXED, kAgent);
+      if (l == 0) {
+        __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
+        __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
+      }
+    }
   }
-
-  if (S == 1) {
-    const int64_t ob = r * a.k;
-    if (mine && rank < a.k) {
-      a.out_idx[ob + rank] = (int32_t)(col_of(x) + a.col_base);
-      a.out_val[ob + rank] = value_bits(x, row);
-    }
-    const int t = threadIdx.x;
-    if (t >= total && t < a.k) {
-      a.out_idx[ob + t] = TK_FILL_IDX;
-      a.out_val[ob + t] = (uint16_t)TK_FILL_VAL;
-    }
-    if (t == 0) {
-      a.out_count[r] = total;
-      a.out_nonfinite[r] = flags;
-    }
-  } else {
-    // agent-scope stores: coherent across the XCDs' caches (see fold_row_if_last)
-    const int64_t sb = r * S + s;
-    if (mine && rank < a.k) __hip_atomic_store(&a.span_list[sb * a.k + rank], x, __ATOMIC_RELAXED, kAgent);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
-      __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
-    }
-    if (a.row_done) fold_row_if_last(a, r, S, row, wave, l);
-  }
+  if (S > 1 && a.row_done) fold_row_if_last(a, r, S, row, wave, l);
 }
 
 // ---------------------------------------------------------------------------
