@@ -335,6 +335,21 @@ tk_status tk_validate_head_bf16(int64_t rows, int64_t hidden, int64_t vocab, int
                                 const uint16_t *logits, int64_t logits_stride);
 
 /*
+ * Releases the scratch the library keeps for `stream` on the current device
+ * (the span lists of split rows, cached per stream between calls) with a
+ * stream-ordered free that follows the work already queued on `stream`, and
+ * forgets the stream.  Call it before destroying a stream that ran top-k
+ * calls with split rows: a stream created later may reuse the handle value,
+ * and would otherwise share the cached buffer (and its arrival counters)
+ * with work still pending from the destroyed one.  A stream the library has
+ * no scratch for returns TK_OK at once; a later call on the stream simply
+ * allocates again.  TK_ERR_DEVICE if HIP fails.  (The library's own: the
+ * pages keep one draft stream per drafter and say nothing of stream
+ * lifetimes.)
+ */
+tk_status tk_release_stream(void *stream);
+
+/*
  * Measurement probe, beside the top-k rather than part of it.  TensorFold PR
  * #713, change 3 measures its span path against a control dispatch in a
  * bench of its own; here the control of a scan's time is the bare read of

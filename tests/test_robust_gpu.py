@@ -202,3 +202,31 @@ def test_read_probe_reads_and_writes_nothing():
     with pytest.raises(tk.TkError) as e:
         tk.read_probe(torch.zeros((9,), dtype=torch.int16, device="cuda"), 4, sink)  # 18 bytes
     assert e.value.status == 2
+
+
+def test_release_stream_then_new_streams():
+    """Split-row calls on a stream, tk_release_stream, the stream destroyed,
+    then new streams (whose handle values may repeat the old one): every call
+    still equals the oracle, and releasing a stream twice, or one the library
+    never saw, is harmless."""
+    import torch
+
+    import wide_row_bf16_amd as tk
+
+    m = family_rows("normal", 15, 98592, 98592, seed=11)
+    want = oracle.topk_bf16(m, 98592, 32)
+    x = upload(m)
+    for i in range(4):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                got = tk.topk_bf16(x, 32)
+            tk.release_stream(s)
+            tk.release_stream(s)
+            again = tk.topk_bf16(x, 32)  # allocates afresh on the same stream
+            tk.release_stream(s)
+        s.synchronize()
+        assert_same(to_numpy(got), want, f"stream {i}")
+        assert_same(to_numpy(again), want, f"stream {i} after release")
+        del s
+    tk.release_stream(torch.cuda.Stream())

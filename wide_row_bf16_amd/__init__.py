@@ -37,7 +37,7 @@ EXPORTS = (
     "tk_validate_f32", "tk_validate_bf16", "tk_topk_bf16_shard", "tk_merge_topk_bf16",
     "tk_validate_merge_bf16", "tk_sample_topk_bf16", "tk_validate_sample_bf16", "tk_head_topk_bf16",
     "tk_validate_head_bf16", "tk_plan_spans", "tk_max_k", "tk_max_span_cols", "tk_status_string", "tk_build_info",
-    "tk_probe_read", "tk_topk_bf16_noalloc",
+    "tk_probe_read", "tk_topk_bf16_noalloc", "tk_release_stream",
 )
 
 
@@ -126,6 +126,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.tk_status_string.argtypes = [i32]
     lib.tk_build_info.restype = ctypes.c_char_p
     lib.tk_build_info.argtypes = []
+    lib.tk_release_stream.restype = i32
+    lib.tk_release_stream.argtypes = [vp]
     lib.tk_probe_read.restype = i32
     lib.tk_probe_read.argtypes = [vp, i64, i32, vp, vp]
     if path == LIBRARY:
@@ -441,3 +443,16 @@ def read_probe(x, workgroups: int, sink) -> None:
                                       _current_stream_handle(torch, dev)))
     if status != TK_OK:
         raise TkError(status, "tk_probe_read")
+
+
+def release_stream(stream=None) -> None:
+    """Frees the scratch the library caches for ``stream`` (a torch.cuda.Stream;
+    default: the current stream) after the work queued on it, before the
+    stream is destroyed (tk_release_stream)."""
+    import torch
+
+    dev = torch.cuda.current_device()
+    handle = stream.cuda_stream if stream is not None else _current_stream_handle(torch, dev)
+    status = int(load().tk_release_stream(handle))
+    if status != TK_OK:
+        raise TkError(status, "tk_release_stream")

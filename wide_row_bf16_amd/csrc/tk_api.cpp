@@ -299,6 +299,17 @@ void *cached_scratch(int dev, hipStream_t stream, size_t bytes, tk_status *st, b
 // between calls; zeroed here whenever the buffer is new).  The stream's cached
 // buffer, or one owned by the call (*owned: the caller frees it,
 // stream-ordered, after its last launch).
+// With g_scratch_mu held: forgets the cached buffer of (dev, stream) after a
+// stream-ordered free, so the next call allocates (and zeroes) a new one.
+void drop_cached(int dev, hipStream_t stream) {
+  for (int i = 0; i < g_scratch_used; ++i) {
+    if (g_scratch[i].dev != dev || g_scratch[i].stream != stream) continue;
+    if (g_scratch[i].ptr) (void)hipFreeAsync(g_scratch[i].ptr, stream);
+    g_scratch[i] = g_scratch[--g_scratch_used];
+    return;
+  }
+}
+
 tk_status acquire_scratch(int dev, hipStream_t stream, size_t total, char **base, bool *owned) {
   tk_status sst = TK_OK;
   bool fresh = false;
@@ -307,7 +318,10 @@ tk_status acquire_scratch(int dev, hipStream_t stream, size_t total, char **base
   *owned = scratch == nullptr;
   if (*owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
   if ((*owned || fresh) && tk::launch_zero_fill((int32_t *)scratch, kFusedMaxRows, stream) != hipSuccess) {
-    if (*owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
+    // already failing: the first error is the one reported.  A cached buffer
+    // whose counters were not zeroed must not be used by a later call.
+    if (*owned) (void)hipFreeAsync(scratch, stream);
+    else drop_cached(dev, stream);
     return TK_ERR_DEVICE;
   }
   *base = (char *)scratch;
@@ -915,20 +929,13 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
   const size_t off_count = align256(off_list + nlists * (size_t)k * sizeof(uint64_t));
   const size_t off_flags = align256(off_count + nlists * sizeof(int32_t));
   const size_t total = align256(off_flags + nlists * sizeof(uint32_t));
-  keep_pool(dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  tk_status sst = TK_OK;
-  bool fresh = false;
-  void *scratch = cached_scratch(dev, stream, total, &sst, &fresh);
+  const Place place{dev, stream, false};
+  auto lock = scratch_lock(place);
+  char *base = nullptr;
+  bool owned = false;
+  const tk_status sst = take_scratch(place, total, &base, &owned);
   if (sst != TK_OK) return sst;
-  const bool owned = scratch == nullptr;
-  if (owned && hipMallocAsync(&scratch, total, stream) != hipSuccess) return TK_ERR_DEVICE;
-  char *base = (char *)scratch;
   int32_t *counters = (int32_t *)base;
-  if ((owned || fresh) && tk::launch_zero_fill(counters, kFusedMaxRows, stream) != hipSuccess) {
-    if (owned) (void)hipFreeAsync(scratch, stream);  // already failing: the first error is the one reported
-    return TK_ERR_DEVICE;
-  }
   tk_status result = TK_OK;
   for (int64_t r0 = 0; r0 < rows; r0 += batch) {
     const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
@@ -948,7 +955,7 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
       break;
     }
   }
-  if (owned && hipFreeAsync(scratch, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
+  if (owned && hipFreeAsync(base, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
   return result;
 }
 
@@ -1120,6 +1127,21 @@ tk_status tk_probe_read(const void *in, int64_t bytes, int32_t workgroups, uint3
   if (overlap(rin, rsink)) return TK_ERR_ALIAS;
   return tk::launch_read_probe(in, bytes / 16, workgroups, sink, (hipStream_t)stream) == hipSuccess ? TK_OK
                                                                                                     : TK_ERR_DEVICE;
+}
+
+tk_status tk_release_stream(void *stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TK_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (int i = 0; i < g_scratch_used; ++i) {
+    if (g_scratch[i].dev != dev || g_scratch[i].stream != (hipStream_t)stream) continue;
+    // stream-ordered: the free waits for the work already queued on the stream
+    const tk_status st =
+        g_scratch[i].ptr && hipFreeAsync(g_scratch[i].ptr, g_scratch[i].stream) != hipSuccess ? TK_ERR_DEVICE : TK_OK;
+    g_scratch[i] = g_scratch[--g_scratch_used];  // forgotten either way: the next call allocates afresh
+    return st;
+  }
+  return TK_OK;
 }
 
 int32_t tk_max_k(void) { return kMaxKWide; }
