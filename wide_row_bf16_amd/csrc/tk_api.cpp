@@ -605,6 +605,11 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
   ha.span_flags = (uint32_t *)(base + off_flags[0]);
   ha.logits = logits;
   ha.logits_stride = logits_stride;
+  // the row sketch lives in the counter words at the buffer's start, zero
+  // between calls (the last merge level zeroes it again); one row tile only
+  uint32_t *sketch = rows <= 16 ? (uint32_t *)(base - off0) : nullptr;
+  static_assert(16 * kMaxK <= kFusedMaxRows, "the sketch fits the counter words");
+  ha.sketch = sketch;
   if (tk::launch_head_scan(ha, stream) != hipSuccess) result = TK_ERR_DEVICE;
   for (int i = 0; i < levels && result == TK_OK; ++i) {
     tk::MergeArgs m{};
@@ -630,9 +635,13 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
       m.out_val = out_val;
       m.out_count = out_count;
       m.out_nonfinite = out_nonfinite;
+      m.sketch = sketch;
     }
     if (tk::launch_span_merge(m, rows, stream) != hipSuccess) result = TK_ERR_DEVICE;
   }
+  // a head kernel that ran without its last merge level leaves the sketch
+  // (the counter words) non-zero: such a cached buffer must not be used again
+  if (result != TK_OK && sketch && !owned) drop_cached(dev, stream);
   if (owned && hipFreeAsync(base - off0, stream) != hipSuccess && result == TK_OK) result = TK_ERR_DEVICE;
   return result;
 }

@@ -220,6 +220,19 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
     load_a(A1, blk + 3);
   }
 
+  // With one row tile, the rows' sketch slots (see HeadArgs) load now, while
+  // the logits are formed: wave w takes rows w, w + 4, ..., lane i slot i.
+  // Agent-scope loads: other XCDs' workgroups write the slots.
+  constexpr int kSketchRows = RT == 1 ? 16 / kHeadWaves : 1;
+  uint32_t slot[kSketchRows];
+#pragma unroll
+  for (int i = 0; i < kSketchRows; ++i) {
+    const int row = wave + i * kHeadWaves;
+    slot[i] = 0;
+    if (RT == 1 && a.sketch && row < a.rows && l < a.k)
+      slot[i] = __hip_atomic_load(&a.sketch[row * a.k + l], __ATOMIC_RELAXED, kAgent);
+  }
+
   // accumulators -> bf16 logits in LDS (and, on request, to memory)
 #pragma unroll
   for (int j = 0; j < kHeadTilesPerWave; ++j) {
@@ -241,7 +254,19 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   // merged in while any beats the k-th kept entry
   const Xchg x = make_xchg();
   const int k = a.k;
+#pragma unroll 1
   for (int row = wave; row < a.rows; row += kHeadWaves) {
+    // The row's floor from its sketch: once all k slots hold a key, k listed
+    // entries (one per slot, from k different spans) reach their minimum, so
+    // a key below it cannot be among the row's k best; equal keys are kept
+    // (the lower column may win).  An empty slot leaves the floor at 0.
+    uint32_t thr = 0;
+    if (RT == 1) {
+      const uint32_t sv = slot[0];
+#pragma unroll
+      for (int i = 0; i + 1 < kSketchRows; ++i) slot[i] = slot[i + 1];  // the next row's slots first
+      if (a.sketch && !ballot(l < k && sv == 0)) thr = wave_min(l < k ? sv : 0xFFFFFFFFu, x);
+    }
     uint32_t c[kHeadLaneCols];
     bool nan = false, ninf = false;
 #pragma unroll
@@ -252,7 +277,7 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
       const uint32_t key = order_key(b);
       nan |= valid && key == 0;
       ninf |= valid && b == 0xFF80u;
-      c[e] = (valid && key) ? (key << 16) | (0xFFFFu - (uint32_t)col) : 0u;
+      c[e] = (valid && key && key >= thr) ? (key << 16) | (0xFFFFu - (uint32_t)col) : 0u;
     }
     uint32_t flags = (ballot(nan) ? kNan : 0u) | (ballot(ninf) ? kNinf : 0u);
     cx(c[0], c[1]); cx(c[2], c[3]); cx(c[0], c[2]); cx(c[1], c[3]); cx(c[1], c[2]);  // descending
@@ -286,6 +311,9 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
     if (l == 0) {
       a.span_count[sb] = cnt;
       a.span_flags[sb] = flags;
+      // this span's best key, the head of its list, into the row's slot
+      if (RT == 1 && a.sketch && cnt > 0)
+        __hip_atomic_fetch_max(&a.sketch[row * k + s % k], list >> 16, __ATOMIC_RELAXED, kAgent);
     }
   }
 }

@@ -812,18 +812,19 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
     c[j] = 0;
     v[j] = 0;
     if (li < n) {
-      c[j] = a.count_in[in_base + li];
+      c[j] = __builtin_amdgcn_readfirstlane(a.count_in[in_base + li]);
       fl |= a.flags_in[in_base + li];
       if (l < k) v[j] = a.list_in[(in_base + li) * k + l];
     }
   }
+  // empty lists (pruned spans of the fused head) are skipped
   uint64_t acc = 0;
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
-    if (wave + j * kWaves >= n) break;
+    if (!c[j]) continue;
     const uint64_t vj = l < c[j] ? v[j] : 0;
-    acc = j == 0 ? vj : merge_sorted64(acc, vj, x);
+    acc = cnt == 0 ? vj : merge_sorted64(acc, vj, x);
     cnt += c[j];
   }
 
@@ -838,8 +839,9 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
   for (int w = 1; w < kWaves; w *= 2) {
     __syncthreads();
     if ((wave & (2 * w - 1)) == 0) {
-      acc = merge_sorted64(acc, s_acc[wave + w][l], x);
-      cnt += s_cnt[wave + w];
+      const int other = __builtin_amdgcn_readfirstlane(s_cnt[wave + w]);
+      if (other) acc = cnt ? merge_sorted64(acc, s_acc[wave + w][l], x) : s_acc[wave + w][l];
+      cnt += other;
       fl |= s_fl[wave + w];
       s_acc[wave][l] = acc;
       if (l == 0) {
@@ -870,6 +872,7 @@ __global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) 
       a.out_count[r] = cnt;
       a.out_nonfinite[r] = flags;
     }
+    if (a.sketch && l < k) a.sketch[r * k + l] = 0;  // zero again for the next call on the stream
   } else {
     const int64_t ob = r * a.lists_out + g;
     if (l < cnt) a.list_out[ob * k + l] = acc;

@@ -78,6 +78,12 @@ struct HeadArgs {
   uint32_t *span_flags;
   uint16_t *logits;
   int64_t logits_stride;
+  // NULL, or [rows][k] key slots, zero at the call's start: a workgroup puts
+  // its span's best key of row r (an entry of its list) into slot (span mod
+  // k) with an atomic max, and one that finds all k slots of a row filled
+  // keeps only keys >= their minimum (k listed entries reach it).  Used with
+  // one row tile (rows <= 16); the last merge level sets the slots to zero.
+  uint32_t *sketch;
 };
 
 hipError_t launch_head_scan(const HeadArgs &a, hipStream_t stream);
@@ -105,6 +111,7 @@ struct MergeArgs {
   int32_t *out_count;
   uint32_t *out_nonfinite;
   int64_t col_base;    // added to every output column index
+  uint32_t *sketch;    // lists_out == 1: [rows][k] words set to zero after the row is written (or NULL)
 };
 
 // Merge of per-shard top-k results: shard g's outputs for all rows are the

@@ -175,3 +175,14 @@ __device__ __forceinline__ uint32_t insert_one(uint32_t list, uint32_t c) {
   const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)list, 0x138, 0xF, 0xF, false);
   return max(list, min(prev, c));
 }
+
+// The minimum of v over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_min(uint32_t v, const Xchg &x) {
+  v = min(v, partner<1>(v, x));
+  v = min(v, partner<2>(v, x));
+  v = min(v, partner<4>(v, x));
+  v = min(v, partner<8>(v, x));
+  v = min(v, partner<16>(v, x));
+  v = min(v, partner<32>(v, x));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
