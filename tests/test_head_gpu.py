@@ -35,6 +35,8 @@ CASES = [
     (12, 1056, 2000, 32, 0, 0, "integers"),
     (15, 2048, 98592, 32, 0, 0, "normal"),
     (64, 1024, 151936, 8, 0, 0, "normal"),
+    (32, 512, 40000, 16, 0, 8, "normal"),  # a multiple of the CU count as spans: 9-10 tiles each
+    (5, 128, 33000, 64, 8, 0, "ties"),  # the same rule at 8-9 tiles a span, ties across spans
     (3, 65536, 300, 8, 0, 0, "normal"),  # the largest hidden: 1024 blocks walked from a rotated start
     (20, 65504, 130, 16, 0, 8, "integers"),  # two row tiles, a half last block, exact sums
 ]

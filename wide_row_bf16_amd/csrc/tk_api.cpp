@@ -553,13 +553,33 @@ tk_status run_wide(int64_t rows, int64_t cols, int64_t stride, int32_t k, const 
   return result;
 }
 
-// Fused head: the head kernel writes one candidate list per (row, span of
-// kHeadSpanCols columns); span_merge_kernel levels (groups of up to
-// kMergeGroup lists, at least one level) fold them into the outputs.
+// Head spans: the vocabulary's 16-column tiles cut into near-equal ranges of
+// at most kHeadSpanCols / 16 tiles, one workgroup each.  By default the
+// spans are full (16 tiles).  Two cases take a multiple of the CU count
+// instead, the smallest whose spans fit, so that every CU holds the same
+// number of workgroups: full spans would put a third workgroup on some CUs
+// (more than 2 x CUs spans: 15 x 2048 x 151936 went from 140.8 to 128.1 us
+// with 768 spans instead of 594), or four row tiles (more than 32 rows,
+// at most two workgroups per CU: 64 x 2048 x 98592, 164.5 -> 157.4 us).
+// With 15 or 32 rows of 98592 columns the 386 full spans measured faster
+// than 512 of 12-13 tiles (82.3 vs 86.3 and 113.5 vs 125.7 us for the head
+// kernel): there the time is set by the bytes the whole grid keeps in
+// flight, which the cut does not change.
+int64_t plan_head(int64_t rows, int64_t vocab, int32_t cus) {
+  constexpr int64_t kTiles = tk::kHeadSpanCols / 16;
+  const int64_t ntiles = (vocab + 15) / 16;
+  const int64_t full = (ntiles + kTiles - 1) / kTiles;
+  if (ntiles < 8 * (int64_t)cus || (full <= 2 * (int64_t)cus && rows <= 32)) return full;
+  return (int64_t)cus * ((ntiles + kTiles * cus - 1) / (kTiles * cus));
+}
+
+// Fused head: the head kernel writes one candidate list per (row, span);
+// span_merge_kernel levels (groups of up to kMergeGroup lists, at least one
+// level) fold them into the outputs.
 tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const uint16_t *h, int64_t h_stride,
                    const uint16_t *w, int64_t w_stride, int32_t *out_idx, uint16_t *out_val, int32_t *out_count,
                    uint32_t *out_nonfinite, uint16_t *logits, int64_t logits_stride, hipStream_t stream, int dev) {
-  const int64_t spans = (vocab + tk::kHeadSpanCols - 1) / tk::kHeadSpanCols;
+  const int64_t spans = plan_head(rows, vocab, device_cus(dev));
   // merge levels: lists in per row at each level; the last level has one
   // group per row (lists_out == 1) and writes the outputs, every earlier level
   // writes the next level's lists (span_merge_kernel tells the two apart by

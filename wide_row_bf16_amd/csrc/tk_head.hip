@@ -12,8 +12,11 @@
 // tk_topk_bf16 on those logits (score descending, lower column first, NaN
 // excluded and flagged, infinities ranked and flagged).
 //
-// Kernel.  One workgroup per span of kHeadSpanCols vocabulary columns, four
-// waves, each owning four 16-column tiles.  The contraction runs on the
+// Kernel.  One workgroup per span of up to kHeadSpanCols vocabulary columns
+// (the host cuts the vocabulary's 16-column tiles into `spans` near-equal
+// ranges), four waves, each owning a contiguous quarter of the span's tiles
+// (four of a full span, three or four of a span of 12 or 13; a missing
+// fourth tile loads nothing and is never written).  The contraction runs on the
 // matrix cores: v_mfma_f32_16x16x32_bf16 with A = a 16-row tile of h and B =
 // 32 hidden values of 16 vocabulary rows of w (each lane loads 16 contiguous
 // bytes of one w row: lane l takes row l % 16, values 8 (l / 16) .. + 7), one
@@ -106,18 +109,29 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   __shared__ __attribute__((aligned(16))) uint8_t s_w[kHeadWaves][kHeadWaveRows * kHeadRowPitch];
 
   const int s = blockIdx.x;
-  const int64_t n0 = (int64_t)s * kHeadSpanCols;
+  const int64_t ntiles = (a.vocab + 15) / 16;
+  const int64_t t0 = ntiles * s / a.spans, t1 = ntiles * (s + 1) / a.spans;  // at most 16 tiles (host)
+  const int64_t n0 = t0 * 16;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = lane_id();
-  const int64_t nvalid = a.vocab - n0 < kHeadSpanCols ? a.vocab - n0 : kHeadSpanCols;
+  const int64_t nvalid = a.vocab - n0 < (t1 - t0) * 16 ? a.vocab - n0 : (t1 - t0) * 16;
 
-  // Both ranges end at the last row's `hidden`-th element, never in its row
+  // This wave's tiles: a contiguous quarter of the span's (at most four).
+  const int nt = (int)(t1 - t0);
+  const int tw0 = wave * nt / kHeadWaves;
+  const int ntw = (wave + 1) * nt / kHeadWaves - tw0;
+  // w's range is the wave's own rows, so the loads of a missing fourth tile
+  // fall outside it and read zeros (an empty range reads nothing).  Both
+  // ranges end at the last row's `hidden`-th element, never in its row
   // padding: the loads below read whole blocks past `hidden`, which the
   // range check turns into zeros on the last row (and which are zeroed in
   // registers on the others).  Ranges and offsets are multiples of 16 bytes
   // (hidden % 32 == 0, strides % 8 == 0), so no load straddles the end.
+  const int64_t wr0 = n0 + 16 * tw0;
+  const int64_t wrows = a.vocab - wr0 < 16 * ntw ? a.vocab - wr0 : 16 * ntw;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.w + n0 * a.w_stride), (short)0, (int)(((nvalid - 1) * a.w_stride + a.hidden) * 2), kBufferWord3);
+      (void *)(a.w + wr0 * a.w_stride), (short)0,
+      wrows > 0 ? (int)(((wrows - 1) * a.w_stride + a.hidden) * 2) : 0, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       (void *)a.h, (short)0, (int)(((a.rows - 1) * a.h_stride + a.hidden) * 2), kBufferWord3);
 
@@ -127,7 +141,6 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int tile0 = wave * kHeadTilesPerWave;
   const int64_t hidden_bytes = a.hidden * 2;
   const int nblk = (int)((hidden_bytes + kHeadBlockBytes - 1) / kHeadBlockBytes);
   // Logical block b reads hidden block (b + rot) mod nblk, rot hashed from the
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   // block loads: instruction q reads kHeadRowsPerLoad wave rows, lane l row
   // q * kHeadRowsPerLoad + l / kHeadLanesPerRow, bytes 16 (l % kHeadLanesPerRow)
   const int lrow = l / kHeadLanesPerRow, lbyte = 16 * (l % kHeadLanesPerRow);
-  const uint32_t g_lane = (uint32_t)(((int64_t)(tile0 * 16 + lrow) * a.w_stride) * 2 + lbyte);
+  const uint32_t g_lane = (uint32_t)(((int64_t)lrow * a.w_stride) * 2 + lbyte);
   const uint32_t g_q = (uint32_t)(kHeadRowsPerLoad * a.w_stride * 2);
   uint8_t *lds_w = s_w[wave];
   const uint32_t st_lane = (uint32_t)(lrow * kHeadRowPitch + lbyte);
@@ -236,7 +249,8 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   // accumulators -> bf16 logits in LDS (and, on request, to memory)
 #pragma unroll
   for (int j = 0; j < kHeadTilesPerWave; ++j) {
-    const int col = (tile0 + j) * 16 + l % 16;
+    if (j >= ntw) break;  // another wave's tile
+    const int col = (tw0 + j) * 16 + l % 16;
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll

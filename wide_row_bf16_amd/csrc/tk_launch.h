@@ -57,8 +57,10 @@ struct ArgmaxArgs {
 
 hipError_t launch_argmax(const ArgmaxArgs &a, int64_t rows_in_launch, hipStream_t stream);
 
-// Fused draft head (tk_head.hip): one workgroup per span of kHeadSpanCols
-// vocabulary columns (spans = ceil(vocab / kHeadSpanCols)); each writes, for
+// Fused draft head (tk_head.hip): one workgroup per span; span s covers the
+// vocabulary's 16-column tiles [ntiles * s / spans, ntiles * (s + 1) / spans)
+// with ntiles = ceil(vocab / 16), at most kHeadSpanCols / 16 of them (the
+// host's choice of spans guarantees it); each writes, for
 // every row, the span's top k as signed composites (key << 32 |
 // (0x7FFFFFFF - column) << 1 | sign) into span_list [rows][spans][k] with
 // counts and flags [rows][spans], for span_merge_kernel (in == NULL) to fold.
