@@ -132,7 +132,7 @@ tk_status tk_topk_bf16_noalloc(int64_t rows, int64_t cols, int64_t row_stride, i
  *          (tk_max_span_cols()) or n > cols (for cols > 0), and for k > 64
  *          when n > 64 (k > 64 splits a row into at most 64 spans, so rows
  *          wider than 64 x tk_max_span_cols() give TK_ERR_SHAPE there).
- *          The automatic plan splits k > 64 rows into at most 8 spans.
+ *          The automatic plan splits k > 64 rows into at most 12 spans.
  *   exact  0 = automatic; 1 = never take the speculative floor (wide spans
  *          otherwise skip elements below a floor estimated from a sample and
  *          verify it afterwards, scanning again when it does not hold).

@@ -469,13 +469,15 @@ tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t 
 }
 
 // 64 < k <= 256: the multi-register scan (tk_wide.hip).  Automatic plans
-// split as for k <= 64 but into at most kWideMaxAutoSpans spans (the fold of
-// a split row merges lists of up to 256 entries); forced plans take up to
+// split as for k <= 64, at most kWideMaxAutoSpans spans (the fold of a split
+// row merges lists of up to 256 entries: on 15 x 98592 rows 12 spans measured
+// 21.5 us at k = 128 and 42.4 us at k = 256 against 22.9 and 43.4 at 8, and
+// 16 x 248320 rows at k = 256 57.7 against 61.6 us); forced plans take up to
 // kMergeGroup spans; rows needing more spans (over 16.7 M columns) are
 // rejected with TK_ERR_SHAPE.  Split rows are always folded by their last
 // workgroup: scratch = the arrival counters, then [batch][S][k] composites,
 // [batch][S] counts and flags.
-constexpr int32_t kWideMaxAutoSpans = 8;
+constexpr int32_t kWideMaxAutoSpans = 12;
 
 int32_t plan_wide(int64_t rows, int64_t cols, int32_t compute_units) {
   int32_t spans = plan(rows, cols, compute_units);

@@ -33,9 +33,10 @@ __device__ __forceinline__ void wide_insert_one(uint32_t (&L)[R], uint32_t c) {
 }
 
 // Merges 64 candidates v (any order, 0 = none) into the list.
+// Merges a descending 64-entry batch v into the R-register list L (the top
+// 64 R of both stay).
 template <int R>
-__device__ __forceinline__ void wide_merge_batch(uint32_t (&L)[R], uint32_t v, const Xchg &x) {
-  v = sort64_desc(v, x);
+__device__ __forceinline__ void wide_merge_sorted(uint32_t (&L)[R], uint32_t v, const Xchg &x) {
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     if (!ballot(v != 0)) break;
@@ -46,6 +47,11 @@ __device__ __forceinline__ void wide_merge_batch(uint32_t (&L)[R], uint32_t v, c
     L[j] = bitonic_merge64_desc(hi, x);
     if (j + 1 < R) v = bitonic_merge64_desc(lo, x);
   }
+}
+
+template <int R>
+__device__ __forceinline__ void wide_merge_batch(uint32_t (&L)[R], uint32_t v, const Xchg &x) {
+  wide_merge_sorted<R>(L, sort64_desc(v, x), x);
 }
 
 template <int R>

@@ -146,6 +146,30 @@ __device__ __forceinline__ uint32_t lane_max_key(const uint4 (&v)[kChunkVecs], u
   return m;
 }
 
+// This lane's two largest order keys in a loaded chunk (same rules as
+// lane_max_key; *m2 is 0 when the lane holds fewer than two keys).  They are
+// distinct elements, so the k-th largest of all lanes' pairs has k elements
+// at or above it: a floor twice as deep as the lane maxima give, which the
+// k > 64 scans need (with k = 256 and 256 lanes the k-th lane maximum is the
+// smallest one).
+__device__ __forceinline__ void lane_top2_keys(const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec, uint32_t inf,
+                                               uint32_t *m1, uint32_t *m2) {
+  uint32_t a = 0, b = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    const bool in = first + (uint32_t)(u * kWave + lane_id()) < nvec;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t key = in ? order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu, inf) : 0u;
+      b = max(b, min(a, key));
+      a = max(a, key);
+    }
+  }
+  *m1 = a;
+  *m2 = b;
+}
+
 __device__ __forceinline__ uint64_t composite64(uint32_t c32, int64_t base) {
   if (!c32) return 0;
   const uint32_t col = (uint32_t)(base + (int64_t)(0xFFFFu - (c32 & 0xFFFFu)));

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   __shared__ int32_t s_count[kWgWaves];
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
-  __shared__ uint32_t s_samp[kWgWaves][kWave];
+  __shared__ uint32_t s_samp[2 * kWgWaves][kWave];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -355,16 +355,33 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
   const uint32_t wn = (uint32_t)(wv1 - wv0);
 
-  // Floors from the workgroup's 256 first-chunk lane maxima, as in the k <= 64
-  // scan: exact = the k-th largest (k lanes hold an element at or above it);
-  // speculative = the spec_rank-th largest (spec_rank < k, chosen on the host
-  // from k and the span width), verified after the scan -- if the lists then
-  // hold k entries, everything dropped is beaten by k kept ones; otherwise the
-  // span is scanned again under the exact floor.
+  // Floors from the workgroup's first chunk, as in the k <= 64 scan: exact =
+  // the k-th largest of the 256 lane maxima (k lanes hold an element at or
+  // above it); speculative = the spec_rank-th largest (spec_rank < k, chosen
+  // on the host from k and the span width), verified after the scan -- if the
+  // lists then hold k entries, everything dropped is beaten by k kept ones;
+  // otherwise the span is scanned again under the exact floor.  With k > 128
+  // and no speculation (few-row splits, whose spans are too short for it) the
+  // k-th lane maximum is nearly the smallest one, so there the exact floor
+  // comes from each lane's two largest keys (512 distinct elements): on
+  // 15 x 98592 rows at k = 256 it admits a fifth of the elements and took the
+  // call from 51.6 to 43.5 us.  Elsewhere the second sort and the extra
+  // merges cost more than they save (k = 128, and every speculating span).
   const Xchg x = make_xchg();
   uint4 A[kChunkVecs];
   if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
-  s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn, a.inf) : 0u, x);
+  const bool speculate =
+      a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks * kChunkVecs * kWave;
+  const bool pairs = R == 4 && a.k > 2 * kWave && !speculate;
+  {
+    uint32_t m1 = 0, m2 = 0;
+    if (wn > 0) {
+      if (pairs) lane_top2_keys(A, 0, wn, a.inf, &m1, &m2);
+      else m1 = lane_max_key(A, 0, wn, a.inf);
+    }
+    s_samp[2 * wave][l] = sort64_desc(m1, x);
+    if (pairs) s_samp[2 * wave + 1][l] = sort64_desc(m2, x);
+  }
   __syncthreads();
   uint32_t exact_floor, spec_floor = 0;
   {
@@ -373,10 +390,11 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int j = 1; j < R; ++j) P[j] = 0;
 #pragma unroll
-    for (int o = 1; o < kWgWaves; ++o) wide_merge_batch<R>(P, s_samp[o][l], x);
+    for (int o = 1; o < 2 * kWgWaves; ++o)
+      if (pairs || (o & 1) == 0) wide_merge_sorted<R>(P, s_samp[o][l], x);
     const uint32_t te = wide_at<R>(P, a.k - 1);
     exact_floor = te > 0 ? te - 1 : 0;
-    if (a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks * kChunkVecs * kWave) {
+    if (speculate) {
       const uint32_t ts = wide_at<R>(P, a.spec_rank - 1);
       spec_floor = ts > 0 ? ts - 1 : 0;
     }
