@@ -33,6 +33,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_stamp_build_is_separate():
+    # the stage-timestamp build is a second library; the product library has
+    # no stamp table and no read-out
+    import ctypes
+    import os
+
+    from wide_row_bf16_amd.build import STAMP_LIBRARY
+
+    assert not hasattr(tk.load(), "tk_stage_stamps")
+    if not os.path.exists(STAMP_LIBRARY):
+        pytest.skip("stamp library not built")
+    stamps = ctypes.CDLL(STAMP_LIBRARY)
+    assert hasattr(stamps, "tk_stage_stamps")
+    stamps.tk_build_info.restype = ctypes.c_char_p
+    assert b"stage-stamps" in stamps.tk_build_info()
+    assert b"stage-stamps" not in tk.load().tk_build_info()
+
+
 def test_constants():
     text = open(HEADER).read()
     assert tk.max_k() == int(re.search(r"#define TK_MAX_K (\d+)u", text).group(1)) == 256

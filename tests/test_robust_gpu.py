@@ -230,3 +230,49 @@ def test_release_stream_then_new_streams():
         assert_same(to_numpy(again), want, f"stream {i} after release")
         del s
     tk.release_stream(torch.cuda.Stream())
+
+
+def test_stamp_build_same_outputs_and_ordered_stages():
+    """The stage-timestamp build (libtk_topk_stamps.so) computes the same
+    outputs as the library, and its table holds ordered stages for a split
+    and an unsplit launch."""
+    import ctypes
+    import os
+
+    import torch
+
+    import wide_row_bf16_amd as tk
+    from wide_row_bf16_amd.build import STAMP_LIBRARY
+
+    if not os.path.exists(STAMP_LIBRARY):
+        pytest.skip("stamp library not built")
+    lib = tk.load(STAMP_LIBRARY)
+    lib.tk_stage_stamps.restype = ctypes.c_int
+    lib.tk_stage_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    stream = torch.cuda.current_stream().cuda_stream
+    for rows, cols, k, spans in ((15, 98592, 32, 12), (6, 40000, 16, 1)):
+        log(f"stamp build rows={rows} cols={cols} k={k} spans={spans}")
+        m = family_rows("normal", rows, cols, seed=rows + k)
+        x = upload(m)
+        want = tk.topk_bf16(x, k, spans=spans)
+        outs = [torch.empty(sh, dtype=dt, device="cuda") for sh, dt in
+                (((rows, k), torch.int32), ((rows, k), torch.int16), ((rows,), torch.int32), ((rows,), torch.int32))]
+        opt = tk.TkOptions(spans=spans, exact=0, general=0)
+        assert lib.tk_topk_bf16_ex(rows, cols, cols, k, x.data_ptr(), *[o.data_ptr() for o in outs], stream,
+                                   ctypes.byref(opt)) == 0
+        torch.cuda.synchronize()
+        assert_same(to_numpy(tk.TopK(*outs)), to_numpy(want), "stamp build vs library")
+        buf = np.zeros(8192 * 16, dtype=np.uint64)
+        assert lib.tk_stage_stamps(buf.ctypes.data, buf.nbytes) == 0
+        t = buf.reshape(8192, 16)[: rows * spans].astype(np.int64)
+        # orders the kernel guarantees (thread 0 stamps 0, 1, 6, 7 in turn; every
+        # wave's body ends after the floor barrier and before the publish one)
+        assert (t[:, 1] >= t[:, 0]).all() and (t[:, 2:6].min(axis=1) >= t[:, 0]).all()
+        assert (t[:, 6] >= t[:, 2:6].max(axis=1)).all() and (t[:, 6] >= t[:, 1]).all()
+        assert (t[:, 7] >= t[:, 6]).all()
+        if spans > 1:
+            last = (t[:, 13] & 1) == 1
+            assert last.sum() == rows
+            assert (t[last, 12] >= t[last, 11]).all() and (t[last, 11] >= t[last, 10]).all()
+            assert (t[last, 10] >= t[last, 9]).all() and (t[:, 9] >= t[:, 8]).all() and (t[:, 8] >= t[:, 7]).all()
+        assert ((t[:, 14] >> 32) < 8).all()  # XCC ids

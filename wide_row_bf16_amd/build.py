@@ -1,4 +1,7 @@
-"""Builds the HIP library libtk_topk.so in-tree for gfx950 with hipcc."""
+"""Builds the HIP library libtk_topk.so in-tree for gfx950 with hipcc, and
+beside it libtk_topk_stamps.so: the same sources with -DTK_STAGE_STAMPS, whose
+scan kernels also record stage timestamps (a measurement build, loaded only
+by bench.py --stage-timeline)."""
 
 from __future__ import annotations
 
@@ -12,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libtk_topk.so")
+STAMP_LIBRARY = os.path.join(PKG, "libtk_topk_stamps.so")
 ARCH = os.environ.get("TK_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,23 +34,35 @@ FLAGS = [
 ]
 
 
-def command(output: str = LIBRARY) -> list[str]:
-    info = f"{ARCH} {' '.join(FLAGS[1:5])}"
+def command(output: str = LIBRARY, stamps: bool = False) -> list[str]:
+    info = f"{ARCH} {' '.join(FLAGS[1:5])}" + (" stage-stamps" if stamps else "")
     return [HIPCC, *FLAGS, "-shared", f"-I{INCLUDE}", f"-I{CSRC}", f'-DTK_BUILD_INFO="{info}"',
-            "-x", "hip", *SOURCES, "-o", output]
+            *(["-DTK_STAGE_STAMPS"] if stamps else []), "-x", "hip", *SOURCES, "-o", output]
 
 
-def build(output: str = LIBRARY, verbose: bool = False) -> str:
-    """Compile the library (always recompiles); returns its path."""
-    tmp = output + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
-    os.replace(tmp, output)
+def build(output: str = LIBRARY, verbose: bool = False, stamps: bool | None = None) -> str:
+    """Compile the library (always recompiles); returns its path.  Building
+    the default library also builds the stamp library beside it, in parallel
+    (stamps=False skips it)."""
+    jobs = [(output, False)]
+    if stamps or (stamps is None and output == LIBRARY):
+        jobs.append((STAMP_LIBRARY, True))
+    procs = []
+    for out, st in jobs:
+        cmd = command(out + ".tmp", st)
+        if verbose:
+            print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = None
+    for out, proc in procs:
+        text, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(text)
+            failed = failed or f"hipcc failed with exit code {proc.returncode} ({os.path.basename(out)})"
+    if failed:
+        raise RuntimeError(failed)
+    for out, _ in procs:
+        os.replace(out + ".tmp", out)
     return output
 
 

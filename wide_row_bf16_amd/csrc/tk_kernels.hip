@@ -35,10 +35,11 @@
 // wave_shr per new entry when few lanes have one, a bitonic sort and merge of
 // 64 when many do.
 //
-// Merge.  The four wave lists meet in LDS; every candidate finds its rank by
-// binary search in the other lists and writes itself at that rank.  With
-// several spans per row, the span lists go to memory and a second kernel folds
-// them pairwise in LDS (a tournament) with the same rank rule.
+// Merge.  The four wave lists, as 64-bit composites, meet as a two-level tree
+// of register bitonic merges.  With several spans per row (up to 64) each
+// workgroup writes its span list to memory and the row's last workgroup to
+// arrive folds the row's lists the same way (fold_row_if_last); above 64
+// spans, and for the fused head, span_merge_kernel folds them in groups.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,6 +47,11 @@
 
 #include "tk_config.h"
 #include "tk_launch.h"
+#include "tk_stamps.h"
+
+#ifdef TK_STAGE_STAMPS
+__device__ uint64_t tk_stamp_table[kStampBlocks * kStampSlots];
+#endif
 
 namespace tk {
 namespace {
@@ -308,10 +314,13 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
   const int64_t rb = r - a.row0;  // the row's counter within this launch
   __builtin_amdgcn_s_waitcnt(0);  // this wave's list stores have completed
   __syncthreads();
+  TK_STAMP(8);
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
   __syncthreads();
+  TK_STAMP(9);
   if (!s_last) return;
+  TK_STAMP_VALUE(13, 1);
   const Xchg x = make_xchg();
   uint64_t acc = 0;
   int cnt = 0;
@@ -346,6 +355,7 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
     s_fl[wave] = fl;
   }
   __syncthreads();
+  TK_STAMP(10);
   // the waves' results as a tree: 0 and 2 take 1 and 3, then 0 takes 2
   if ((wave & 1) == 0) {
     acc = merge_sorted64(acc, s_acc[wave + 1][l], x);
@@ -364,6 +374,7 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
     acc = merge_sorted64(acc, s_acc[2][l], x);
     cnt += s_cnt[2];
     fl |= s_fl[2];
+    TK_STAMP(11);
     const int k = a.k;
     if (cnt > k) cnt = k;
     const int64_t ob = r * k;
@@ -381,6 +392,7 @@ __device__ __forceinline__ void fold_row_if_last(const ScanArgs &a, int64_t r, i
       a.out_nonfinite[r] = fl;
       __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
     }
+    TK_STAMP(12);
   }
 }
 
@@ -398,6 +410,9 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));  // uniform per wave
   const int l = lane_id();
   const uint16_t *row = a.in + r * a.stride;
+  TK_STAMP(0);
+  TK_STAMP_HW(14);
+  TK_STAMP_VALUE(13, 0);
 
   // The row's 16-byte grid: vector j covers columns [a0 + 8j, a0 + 8j + 8).
   const int64_t a0 = (int64_t)((8u - (uint32_t)(((uintptr_t)row >> 1) & 7u)) & 7u);
@@ -464,6 +479,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     floor = spec_floor;
     verify = true;
   }
+  TK_STAMP(1);
 
   int total = 0;
   uint32_t flags = 0;
@@ -486,6 +502,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     if (wave == 0 && head_hi > head_lo) take_columns(w, row, head_lo, head_hi, base);
     if (wn > 0) take_body(w, wvp, wn, a0 + kVecElems * wv0, base, A);
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns(w, row, tail_lo, tail_hi, base);
+    TK_WAVE_STAMP(2 + wave);
 
     // publish this wave's list
     const uint64_t valid_mask = ballot(w.list != 0);
@@ -496,6 +513,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
       s_flags[wave] = w.flags | ((readlane(w.list, 0) >> 16) == 0x8000u + a.inf ? kPinf : 0u);
     }
     __syncthreads();
+    TK_STAMP(6);
 
     total = 0;
     flags = 0;
@@ -546,6 +564,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
         __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
       }
     }
+    TK_STAMP(7);
   }
   if (S > 1 && a.row_done) fold_row_if_last(a, r, S, row, wave, l);
 }
@@ -977,6 +996,8 @@ __global__ __launch_bounds__(kWgThreads) void read_probe_kernel(const uint4 *in,
   const int64_t w0 = j0 + (j1 - j0) * wave / kWgWaves, w1 = j0 + (j1 - j0) * (wave + 1) / kWgWaves;
   const uint32_t wn = (uint32_t)(w1 - w0);
   uint32_t acc = 0;
+  TK_STAMP(0);
+  TK_STAMP_HW(14);
   auto fold = [&](const uint4 (&v)[kChunkVecs]) {
 #pragma unroll
     for (int u = 0; u < kChunkVecs; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -995,6 +1016,7 @@ __global__ __launch_bounds__(kWgThreads) void read_probe_kernel(const uint4 *in,
     }
   }
   if (acc == 0x9E3779B9u) sink[b & 8191] = acc;
+  TK_WAVE_STAMP(2 + wave);  // after the last fold: every load of the wave has returned
 }
 
 hipError_t launch_read_probe(const void *in, int64_t nvec, int32_t workgroups, uint32_t *sink, hipStream_t stream) {
@@ -1066,3 +1088,12 @@ hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStre
 }
 
 }  // namespace tk
+
+#ifdef TK_STAGE_STAMPS
+// Copies the stage table of the last stamped launches (bytes at most its
+// size); synchronous.  Present in the stamp build only.
+extern "C" int tk_stage_stamps(void *dst, size_t bytes) {
+  if (bytes > sizeof(tk_stamp_table)) return 1;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(tk_stamp_table), bytes) == hipSuccess ? 0 : 1;
+}
+#endif
