@@ -49,10 +49,6 @@
 #include "tk_launch.h"
 #include "tk_stamps.h"
 
-#ifdef TK_STAGE_STAMPS
-__device__ uint64_t tk_stamp_table[kStampBlocks * kStampSlots];
-#endif
-
 namespace tk {
 namespace {
 

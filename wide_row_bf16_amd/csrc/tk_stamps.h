@@ -3,7 +3,10 @@
 // below is empty).  A stamped kernel records, per workgroup (the first
 // kStampBlocks of a launch), the 100 MHz real-time counter at the stages of
 // its path and its hardware ids; tk_stage_stamps() copies the table out after
-// the launch.  Slots of a workgroup (uint64 each):
+// the launch.  Each translation unit that includes this header has its own
+// table (device symbols do not cross units without relocatable device
+// code): tk_kernels.hip's read-out is tk_stage_stamps, tk_wide.hip's
+// tk_stage_stamps_wide.  Slots of a workgroup (uint64 each):
 //   0 start                 1 floors computed          2..5 wave w's body done
 //   6 lists published       7 merge done, written      8 stores completed (split rows)
 //   9 arrival counted       10 last arrival: lists loaded and folded per wave
@@ -15,7 +18,7 @@
 #ifdef TK_STAGE_STAMPS
 constexpr int kStampBlocks = 8192;
 constexpr int kStampSlots = 16;
-extern __device__ uint64_t tk_stamp_table[kStampBlocks * kStampSlots];
+static __device__ uint64_t tk_stamp_table[kStampBlocks * kStampSlots];
 
 __device__ __forceinline__ void tk_stamp_put(int slot, uint64_t v) {
   if (blockIdx.x < (uint32_t)kStampBlocks) tk_stamp_table[blockIdx.x * kStampSlots + slot] = v;

@@ -31,6 +31,7 @@
 
 #include "tk_config.h"
 #include "tk_launch.h"
+#include "tk_stamps.h"
 
 namespace tk {
 namespace {
@@ -241,10 +242,13 @@ __device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, 
   const int64_t rb = r - a.row0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  TK_STAMP(8);
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(&a.row_done[rb], 1, __ATOMIC_RELAXED, kAgent) == S - 1;
   __syncthreads();
+  TK_STAMP(9);
   if (!s_last) return;
+  TK_STAMP_VALUE(13, 1);
   const Xchg x = make_xchg();
   const int k = a.k;
   uint64_t acc[R];
@@ -252,22 +256,32 @@ __device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, 
   for (int j = 0; j < R; ++j) acc[j] = 0;
   int cnt = 0;
   uint32_t fl = 0;
-  for (int i = wave; i < S; i += kWgWaves) {
-    const int64_t sb = r * S + i;
-    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent);
-    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
-    uint64_t B[R];
+  // each wave folds lists wave, wave + 4, ...; four lists' loads in flight at once
+  for (int i0 = wave; i0 < S; i0 += 4 * kWgWaves) {
+    uint64_t B[4][R];
+    int c[4];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int e = j * kWave + l;
-      B[j] = e < c ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * kWgWaves;
+      const int64_t sb = r * S + i;
+      c[q] = i < S ? __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent) : 0;
+      if (i < S) fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int e = j * kWave + l;
+        B[q][j] = e < c[q] ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+      }
     }
-    cnt += c;
-    if (i == wave) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[j] = B[j];
-    } else {
-      wide_merge_lists64<R>(acc, B, x);
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q * kWgWaves >= S) break;
+      cnt += c[q];
+      if (i0 == wave && q == 0) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[j] = B[q][j];
+      } else {
+        wide_merge_lists64<R>(acc, B[q], x);
+      }
     }
   }
 #pragma unroll
@@ -277,6 +291,7 @@ __device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, 
     s_fl[wave] = fl;
   }
   __syncthreads();
+  TK_STAMP(10);
 #pragma unroll
   for (int step = 1; step < kWgWaves; step *= 2) {
     if (wave % (2 * step) == 0) {
@@ -290,6 +305,7 @@ __device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, 
     __syncthreads();
   }
   if (wave != 0) return;
+  TK_STAMP(11);
 #pragma unroll
   for (int o = 1; o < kWgWaves; ++o) {
     cnt += s_cnt[o];
@@ -315,6 +331,7 @@ __device__ __forceinline__ void wide_fold_if_last(const ScanArgs &a, int64_t r, 
     a.out_nonfinite[r] = fl;
     __hip_atomic_store(&a.row_done[rb], 0, __ATOMIC_RELAXED, kAgent);
   }
+  TK_STAMP(12);
 }
 
 template <int R>
@@ -332,6 +349,9 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const uint16_t *row = a.in + r * a.stride;
+  TK_STAMP(0);
+  TK_STAMP_HW(14);
+  TK_STAMP_VALUE(13, 0);
 
   // the span and wave shares of the k <= 64 scan
   const int64_t a0 = (int64_t)((8u - (uint32_t)(((uintptr_t)row >> 1) & 7u)) & 7u);
@@ -385,13 +405,30 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   __syncthreads();
   uint32_t exact_floor, spec_floor = 0;
   {
+    // P = the top 64 R of the sorted lists, as a tree of bitonic merges:
+    // 64 + 64 -> 128, then 128 + 128 -> 256 (and with pairs, the top 256 of
+    // two such 256s)
     uint32_t P[R];
-    P[0] = s_samp[0][l];
+    uint32_t Q[4][2];
 #pragma unroll
-    for (int j = 1; j < R; ++j) P[j] = 0;
-#pragma unroll
-    for (int o = 1; o < 2 * kWgWaves; ++o)
-      if (pairs || (o & 1) == 0) wide_merge_sorted<R>(P, s_samp[o][l], x);
+    for (int i = 0; i < 4; ++i) {
+      if (i >= 2 && !pairs) break;
+      const int o0 = pairs ? 2 * i : 4 * i, o1 = pairs ? 2 * i + 1 : 4 * i + 2;
+      const uint32_t a1[1] = {s_samp[o0][l]}, b1[1] = {s_samp[o1][l]};
+      wide_merge_full<1>(a1, b1, Q[i], x);
+    }
+    if constexpr (R == 2) {
+      P[0] = Q[0][0];
+      P[1] = Q[0][1];
+      wide_merge_top<2>(P, Q[1], x);
+    } else {
+      wide_merge_full<2>(Q[0], Q[1], P, x);
+      if (pairs) {
+        uint32_t V[4];
+        wide_merge_full<2>(Q[2], Q[3], V, x);
+        wide_merge_top<4>(P, V, x);
+      }
+    }
     const uint32_t te = wide_at<R>(P, a.k - 1);
     exact_floor = te > 0 ? te - 1 : 0;
     if (speculate) {
@@ -405,6 +442,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
     floor = spec_floor;
     verify = true;
   }
+  TK_STAMP(1);
 
   WaveWide<R> w;
   int total = 0;
@@ -449,6 +487,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       }
     }
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) wide_columns<R>(w, row, tail_lo, tail_hi, base);
+    TK_WAVE_STAMP(2 + wave);
 
     // the wave's list, its count and flags to LDS
     int cnt = 0;
@@ -462,6 +501,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       s_flags[wave] = w.flags | ((readlane(w.L[0], 0) >> 16) == 0x8000u + a.inf ? kPinf : 0u);
     }
     __syncthreads();
+    TK_STAMP(6);
     total = 0;
     flags = 0;
 #pragma unroll
@@ -506,12 +546,14 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       a.out_count[r] = total;
       a.out_nonfinite[r] = flags;
     }
+    TK_STAMP(7);
     return;
   }
   if (threadIdx.x == 0) {
     __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
     __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
   }
+  TK_STAMP(7);
   // the rank merge's reads of s_list are done once every wave has passed this
   // point; the fold then reuses s_list as its exchange buffer
   __syncthreads();
@@ -532,3 +574,12 @@ hipError_t launch_wide_scan(const ScanArgs &a, int64_t rows_in_launch, hipStream
 }
 
 }  // namespace tk
+
+#ifdef TK_STAGE_STAMPS
+// Copies the stage table of the last stamped wide-scan launches (bytes at
+// most its size); synchronous.  Present in the stamp build only.
+extern "C" int tk_stage_stamps_wide(void *dst, size_t bytes) {
+  if (bytes > sizeof(tk_stamp_table)) return 1;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(tk_stamp_table), bytes) == hipSuccess ? 0 : 1;
+}
+#endif
