@@ -517,32 +517,52 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   }
   if (total > a.k) total = a.k;
 
-  // rank of each kept entry in the union of the four lists
+  // The four wave lists meet as a tree of register merges (as in the k <= 64
+  // scan): waves 0 and 2 merge the next wave's list into theirs, then wave 0
+  // merges in wave 2's result and writes the top k.  A wave's entries past
+  // its count are empty zeros or beaten by k of its own, so they can only
+  // land at merged ranks >= k and whole lists are merged.  (Ranking every
+  // entry by binary searches in the other three lists read ~200 KB of LDS
+  // per workgroup at k = 256.)
   const int64_t sb = r * S + s;
+  uint64_t acc[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int e = j * kWave + l;
-    if (e >= s_count[wave]) continue;
-    const uint64_t xv = s_list[wave][e];
-    int rank = e;
+  for (int j = 0; j < R; ++j) acc[j] = s_list[wave][j * kWave + l];
+  if ((wave & 1) == 0) {
+    uint64_t B[R];
 #pragma unroll
-    for (int o = 0; o < kWgWaves; ++o)
-      if (o != wave) rank += count_beating(s_list[o], s_count[o], xv);
-    if (rank >= a.k) continue;
-    if (S == 1) {
-      a.out_idx[r * a.k + rank] = (int32_t)(col_of(xv) + a.col_base);
-      a.out_val[r * a.k + rank] = value_bits(xv, row);
-    } else {
-      __hip_atomic_store(&a.span_list[sb * a.k + rank], xv, __ATOMIC_RELAXED, kAgent);
+    for (int j = 0; j < R; ++j) B[j] = s_list[wave + 1][j * kWave + l];
+    wide_merge_lists64<R>(acc, B, x);
+  }
+  if (wave == 2) {  // no other wave reads slot 2 before the barrier
+#pragma unroll
+    for (int j = 0; j < R; ++j) s_list[2][j * kWave + l] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t B[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) B[j] = s_list[2][j * kWave + l];
+    wide_merge_lists64<R>(acc, B, x);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = j * kWave + l;
+      if (e >= a.k) break;
+      if (S == 1) {
+        if (e < total) {
+          a.out_idx[r * a.k + e] = (int32_t)(col_of(acc[j]) + a.col_base);
+          a.out_val[r * a.k + e] = value_bits(acc[j], row);
+        } else {
+          a.out_idx[r * a.k + e] = TK_FILL_IDX;
+          a.out_val[r * a.k + e] = (uint16_t)TK_FILL_VAL;
+        }
+      } else if (e < total) {
+        __hip_atomic_store(&a.span_list[sb * a.k + e], acc[j], __ATOMIC_RELAXED, kAgent);
+      }
     }
   }
   if (S == 1) {
-    const int t = threadIdx.x;
-    if (t >= total && t < a.k) {
-      a.out_idx[r * a.k + t] = TK_FILL_IDX;
-      a.out_val[r * a.k + t] = (uint16_t)TK_FILL_VAL;
-    }
-    if (t == 0) {
+    if (threadIdx.x == 0) {
       a.out_count[r] = total;
       a.out_nonfinite[r] = flags;
     }
@@ -554,7 +574,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
     __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
   }
   TK_STAMP(7);
-  // the rank merge's reads of s_list are done once every wave has passed this
+  // the merge tree's reads of s_list are done once every wave has passed this
   // point; the fold then reuses s_list as its exchange buffer
   __syncthreads();
   wide_fold_if_last<R>(a, r, S, row, wave, l, s_list);
