@@ -15,9 +15,10 @@
 // (row, span), a per-wave list of the 64 best composites in registers, one
 // lane per entry, a raw-bit filter that skips vectors without a candidate,
 // floors from a pooled first-chunk sample, thresholds shared in LDS, issue
-// priority falling with progress, a rank merge in LDS, and the last
-// workgroup of a split row folding the span lists), with four fp32 elements
-// per 16-byte vector and 64-bit list entries.
+// priority falling with progress, the four wave lists meeting as a tree of
+// register merges, and the last workgroup of a split row folding the span
+// lists), with four fp32 elements per 16-byte vector and 64-bit list
+// entries.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -307,16 +308,6 @@ __device__ __forceinline__ uint32_t value_bits32(uint64_t x, const uint32_t *row
   return row[col_of32(x)];
 }
 
-__device__ __forceinline__ int count_beating32(const uint64_t *list, int n, uint64_t x) {
-  int lo = 0, hi = n;  // entries [0, lo) beat x, [hi, n) do not
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] > x) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // The last workgroup of a split row folds the row's span lists (see
 // fold_row_if_last in the bf16 scan: agent-scope atomic stores and loads, an
 // arrival counter that returns to zero).
@@ -337,14 +328,29 @@ __device__ __forceinline__ void fold_row32_if_last(const ScanArgs32 &a, int64_t 
   uint64_t acc = 0;
   int cnt = 0;
   uint32_t fl = 0;
-  for (int i = wave; i < S; i += kWgWaves) {
-    const int64_t sb = r * S + i;
-    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t v =
-        l < c ? __hip_atomic_load(&a.span_list[sb * a.k + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-    acc = i == wave ? v : merge_sorted64(acc, v, x);
-    cnt += c;
+  // each wave folds lists wave, wave + 4, ...; four lists' loads in flight at once
+  for (int i0 = wave; i0 < S; i0 += 4 * kWgWaves) {
+    uint64_t v[4];
+    int c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * kWgWaves;
+      const int64_t sb = r * S + i;
+      c[q] = 0;
+      v[q] = 0;
+      if (i < S) {
+        c[q] = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (l < a.k) v[q] = __hip_atomic_load(&a.span_list[sb * a.k + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q * kWgWaves >= S) break;
+      const uint64_t vq = l < c[q] ? v[q] : 0;
+      acc = (i0 == wave && q == 0) ? vq : merge_sorted64(acc, vq, x);
+      cnt += c[q];
+    }
   }
   s_acc[wave][l] = acc;
   if (l == 0) {
@@ -352,13 +358,24 @@ __device__ __forceinline__ void fold_row32_if_last(const ScanArgs32 &a, int64_t 
     s_fl[wave] = fl;
   }
   __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int o = 1; o < kWgWaves; ++o) {
-    acc = merge_sorted64(acc, s_acc[o][l], x);
-    cnt += s_cnt[o];
-    fl |= s_fl[o];
+  // the waves' results as a tree: 0 and 2 take 1 and 3, then 0 takes 2
+  if ((wave & 1) == 0) {
+    acc = merge_sorted64(acc, s_acc[wave + 1][l], x);
+    cnt += s_cnt[wave + 1];
+    fl |= s_fl[wave + 1];
   }
+  if (wave == 2) {
+    s_acc[2][l] = acc;
+    if (l == 0) {
+      s_cnt[2] = cnt;
+      s_fl[2] = fl;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  acc = merge_sorted64(acc, s_acc[2][l], x);
+  cnt += s_cnt[2];
+  fl |= s_fl[2];
   const int k = a.k;
   if (cnt > k) cnt = k;
   const int64_t ob = r * k;
@@ -488,40 +505,40 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
   }
   if (total > a.k) total = a.k;
 
-  const uint64_t x = s_list[wave][l];
-  const bool mine = l < s_count[wave];
-  int rank = l;
-  if (mine) {
-#pragma unroll
-    for (int o = 0; o < kWgWaves; ++o)
-      if (o != wave) rank += count_beating32(s_list[o], s_count[o], x);
+  // The four wave lists meet as a tree in registers (as in the 16-bit scan):
+  // waves 0 and 2 merge the next wave's list into theirs, then wave 0 merges
+  // in wave 2's result.  Entries past a wave's count are empty zeros or
+  // beaten by k of its own, so whole lists are merged.
+  const Xchg xm = make_xchg();
+  uint64_t acc = s_list[wave][l];
+  if ((wave & 1) == 0) acc = merge_sorted64(acc, s_list[wave + 1][l], xm);
+  if (wave == 2) s_list[2][l] = acc;  // no other wave reads slot 2 before the barrier
+  __syncthreads();
+  if (wave == 0) {
+    acc = merge_sorted64(acc, s_list[2][l], xm);
+    if (S == 1) {
+      const int64_t ob = r * a.k;
+      if (l < total) {
+        a.out_idx[ob + l] = col_of32(acc);
+        a.out_val[ob + l] = value_bits32(acc, row);
+      } else if (l < a.k) {
+        a.out_idx[ob + l] = TK_FILL_IDX;
+        a.out_val[ob + l] = 0x7FC00000u;
+      }
+      if (l == 0) {
+        a.out_count[r] = total;
+        a.out_nonfinite[r] = flags;
+      }
+    } else {
+      const int64_t sb = r * S + s;
+      if (l < total) __hip_atomic_store(&a.span_list[sb * a.k + l], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (l == 0) {
+        __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
-
-  if (S == 1) {
-    const int64_t ob = r * a.k;
-    if (mine && rank < a.k) {
-      a.out_idx[ob + rank] = col_of32(x);
-      a.out_val[ob + rank] = value_bits32(x, row);
-    }
-    const int t = threadIdx.x;
-    if (t >= total && t < a.k) {
-      a.out_idx[ob + t] = TK_FILL_IDX;
-      a.out_val[ob + t] = 0x7FC00000u;
-    }
-    if (t == 0) {
-      a.out_count[r] = total;
-      a.out_nonfinite[r] = flags;
-    }
-  } else {
-    const int64_t sb = r * S + s;
-    if (mine && rank < a.k)
-      __hip_atomic_store(&a.span_list[sb * a.k + rank], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    fold_row32_if_last(a, r, S, row, wave, l);
-  }
+  if (S > 1) fold_row32_if_last(a, r, S, row, wave, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -888,22 +905,32 @@ __device__ __forceinline__ void wide32_fold_if_last(const ScanArgs32 &a, int64_t
   for (int j = 0; j < R; ++j) acc[j] = 0;
   int cnt = 0;
   uint32_t fl = 0;
-  for (int i = wave; i < S; i += kWgWaves) {
-    const int64_t sb = r * S + i;
-    const int c = __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent);
-    fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
-    uint64_t B[R];
+  // each wave folds lists wave, wave + 4, ...; four lists' loads in flight at once
+  for (int i0 = wave; i0 < S; i0 += 4 * kWgWaves) {
+    uint64_t B[4][R];
+    int c[4];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int e = j * kWave + l;
-      B[j] = e < c ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * kWgWaves;
+      const int64_t sb = r * S + i;
+      c[q] = i < S ? __hip_atomic_load(&a.span_count[sb], __ATOMIC_RELAXED, kAgent) : 0;
+      if (i < S) fl |= __hip_atomic_load(&a.span_flags[sb], __ATOMIC_RELAXED, kAgent);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int e = j * kWave + l;
+        B[q][j] = e < c[q] ? __hip_atomic_load(&a.span_list[sb * k + e], __ATOMIC_RELAXED, kAgent) : 0;
+      }
     }
-    cnt += c;
-    if (i == wave) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[j] = B[j];
-    } else {
-      wide_merge_lists64<R>(acc, B, x);
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q * kWgWaves >= S) break;
+      cnt += c[q];
+      if (i0 == wave && q == 0) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[j] = B[q][j];
+      } else {
+        wide_merge_lists64<R>(acc, B[q], x);
+      }
     }
   }
 #pragma unroll
@@ -999,12 +1026,22 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   __syncthreads();
   uint32_t exact_floor, spec_floor = 0;
   {
+    // P = the top 64 R of the four sorted lists: 64 + 64 -> 128, then
+    // 128 + 128 -> 256 (or its top 128), as bitonic merges
     uint32_t P[R];
-    P[0] = s_samp[0][l];
-#pragma unroll
-    for (int j = 1; j < R; ++j) P[j] = 0;
-#pragma unroll
-    for (int o = 1; o < kWgWaves; ++o) wide_merge_batch<R>(P, s_samp[o][l], x);
+    uint32_t Q0[2], Q1[2];
+    {
+      const uint32_t l0[1] = {s_samp[0][l]}, l1[1] = {s_samp[1][l]}, l2[1] = {s_samp[2][l]}, l3[1] = {s_samp[3][l]};
+      wide_merge_full<1>(l0, l1, Q0, x);
+      wide_merge_full<1>(l2, l3, Q1, x);
+    }
+    if constexpr (R == 2) {
+      P[0] = Q0[0];
+      P[1] = Q0[1];
+      wide_merge_top<2>(P, Q1, x);
+    } else {
+      wide_merge_full<2>(Q0, Q1, P, x);
+    }
     const uint32_t te = wide_at<R>(P, a.k - 1);
     exact_floor = te > 0 ? te - 1 : 0;
     if (a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks32 * kChunkVecs * kWave) {
@@ -1067,31 +1104,47 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   }
   if (total > a.k) total = a.k;
 
+  // the four wave lists meet as a tree of register merges (see the 16-bit
+  // scan): waves 0 and 2 take the next wave's list, wave 0 then wave 2's
   const int64_t sb = r * S + s;
+  uint64_t acc[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int e = j * kWave + l;
-    if (e >= s_count[wave]) continue;
-    const uint64_t xv = s_list[wave][e];
-    int rank = e;
+  for (int j = 0; j < R; ++j) acc[j] = s_list[wave][j * kWave + l];
+  if ((wave & 1) == 0) {
+    uint64_t B[R];
 #pragma unroll
-    for (int o = 0; o < kWgWaves; ++o)
-      if (o != wave) rank += count_beating32(s_list[o], s_count[o], xv);
-    if (rank >= a.k) continue;
-    if (S == 1) {
-      a.out_idx[r * a.k + rank] = col_of32(xv);
-      a.out_val[r * a.k + rank] = value_bits32(xv, row);
-    } else {
-      __hip_atomic_store(&a.span_list[sb * a.k + rank], xv, __ATOMIC_RELAXED, kAgent);
+    for (int j = 0; j < R; ++j) B[j] = s_list[wave + 1][j * kWave + l];
+    wide_merge_lists64<R>(acc, B, x);
+  }
+  if (wave == 2) {  // no other wave reads slot 2 before the barrier
+#pragma unroll
+    for (int j = 0; j < R; ++j) s_list[2][j * kWave + l] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t B[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) B[j] = s_list[2][j * kWave + l];
+    wide_merge_lists64<R>(acc, B, x);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = j * kWave + l;
+      if (e >= a.k) break;
+      if (S == 1) {
+        if (e < total) {
+          a.out_idx[r * a.k + e] = col_of32(acc[j]);
+          a.out_val[r * a.k + e] = value_bits32(acc[j], row);
+        } else {
+          a.out_idx[r * a.k + e] = TK_FILL_IDX;
+          a.out_val[r * a.k + e] = 0x7FC00000u;
+        }
+      } else if (e < total) {
+        __hip_atomic_store(&a.span_list[sb * a.k + e], acc[j], __ATOMIC_RELAXED, kAgent);
+      }
     }
   }
   if (S == 1) {
-    const int t = threadIdx.x;
-    if (t >= total && t < a.k) {
-      a.out_idx[r * a.k + t] = TK_FILL_IDX;
-      a.out_val[r * a.k + t] = 0x7FC00000u;
-    }
-    if (t == 0) {
+    if (threadIdx.x == 0) {
       a.out_count[r] = total;
       a.out_nonfinite[r] = flags;
     }
@@ -1101,7 +1154,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
     __hip_atomic_store(&a.span_count[sb], total, __ATOMIC_RELAXED, kAgent);
     __hip_atomic_store(&a.span_flags[sb], flags, __ATOMIC_RELAXED, kAgent);
   }
-  __syncthreads();  // the rank merge's reads of s_list are done; the fold reuses it
+  __syncthreads();  // the merge tree's reads of s_list are done; the fold reuses it
   wide32_fold_if_last<R>(a, r, S, row, wave, l, s_list);
 }
 

@@ -187,17 +187,6 @@ __device__ __forceinline__ uint16_t value_bits(uint64_t x, const uint16_t *row) 
   return row[col_of(x)];
 }
 
-// Number of entries of the descending list[0, n) that beat x.
-__device__ __forceinline__ int count_beating(const uint64_t *list, int n, uint64_t x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] > x) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // Signed composites key << 32 | (0x7FFFFFFF - column) << 1 | sign: the same
 // order as the plain ones for distinct columns, and the value's sign bit
 // carried along, so an entry's bits come back without the input (-0 and +0

@@ -20,12 +20,13 @@
 //    Registers whose last entry already beats the batch's first are skipped.
 // The filter, the trip masks, the chunk loads and the flags are those of the
 // k <= 64 scan.  The exact floor is the k-th largest of the 256 lane maxima
-// of each wave's first chunk (k lanes hold an element at or above it); a
-// speculative floor (a lower rank of the same sample, verified after the scan
-// and followed by a rescan under the exact floor when it fails) spares most of
-// the insertions on wide spans.  The four wave lists meet in LDS by rank
-// (binary search in the other lists); split rows are folded by their last
-// workgroup with 64-bit list merges.
+// of each wave's first chunk (k lanes hold an element at or above it; on
+// few-row splits at k > 128, of each lane's two largest keys); a speculative
+// floor (a lower rank of the same sample, verified after the scan and
+// followed by a rescan under the exact floor when it fails) spares most of
+// the insertions on wide spans.  The four wave lists meet as a tree of
+// bitonic list merges in registers; split rows are folded by their last
+// workgroup with the same 64-bit list merges.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
