@@ -226,6 +226,26 @@ __device__ __forceinline__ uint32_t lane_max_key32(const uint4 (&v)[kChunkVecs],
   return m;
 }
 
+// This lane's two largest keys in a loaded chunk (*m2 = 0 with fewer than
+// two): distinct elements, for the deeper floor of few-row k > 128 splits.
+__device__ __forceinline__ void lane_top2_keys32(const uint4 (&v)[kChunkVecs], uint32_t nvec, uint32_t *m1,
+                                                 uint32_t *m2) {
+  uint32_t a = 0, b = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const bool in = (uint32_t)(u * kWave + lane_id()) < nvec;
+    const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t key = in ? key32(e[i]) : 0u;
+      b = max(b, min(a, key));
+      a = max(a, key);
+    }
+  }
+  *m1 = a;
+  *m2 = b;
+}
+
 // One chunk: trips against the thresholds at its start (they only rise),
 // then the exact path for the tripped vectors in order.
 __device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
@@ -986,7 +1006,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   __shared__ int32_t s_count[kWgWaves];
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
-  __shared__ uint32_t s_samp[kWgWaves][kWave];
+  __shared__ uint32_t s_samp[2 * kWgWaves][kWave];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -1017,34 +1037,55 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   const uint4 *wvp = reinterpret_cast<const uint4 *>(row + a0) + wv0;
   const uint32_t wn = (uint32_t)(wv1 - wv0);
 
-  // floors from the workgroup's 256 first-chunk lane maxima (R-register merge:
-  // k may exceed one register)
+  // floors from the workgroup's first chunk (R-register lists: k may exceed
+  // one register): the lane maxima, or -- with k > 128 and no speculation,
+  // where the k-th lane maximum is nearly the smallest -- each lane's two
+  // largest keys (see the 16-bit wide scan)
   const Xchg x = make_xchg();
   uint4 A[kChunkVecs];
   if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
-  s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key32(A, wn) : 0u, x);
+  const bool speculate =
+      a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks32 * kChunkVecs * kWave;
+  const bool pairs = R == 4 && a.k > 2 * kWave && !speculate;
+  {
+    uint32_t m1 = 0, m2 = 0;
+    if (wn > 0) {
+      if (pairs) lane_top2_keys32(A, wn, &m1, &m2);
+      else m1 = lane_max_key32(A, wn);
+    }
+    s_samp[2 * wave][l] = sort64_desc(m1, x);
+    if (pairs) s_samp[2 * wave + 1][l] = sort64_desc(m2, x);
+  }
   __syncthreads();
   uint32_t exact_floor, spec_floor = 0;
   {
-    // P = the top 64 R of the four sorted lists: 64 + 64 -> 128, then
-    // 128 + 128 -> 256 (or its top 128), as bitonic merges
+    // P = the top 64 R of the sorted lists, as a tree of bitonic merges:
+    // 64 + 64 -> 128, then 128 + 128 -> 256 (and with pairs, the top 256 of
+    // two such 256s)
     uint32_t P[R];
-    uint32_t Q0[2], Q1[2];
-    {
-      const uint32_t l0[1] = {s_samp[0][l]}, l1[1] = {s_samp[1][l]}, l2[1] = {s_samp[2][l]}, l3[1] = {s_samp[3][l]};
-      wide_merge_full<1>(l0, l1, Q0, x);
-      wide_merge_full<1>(l2, l3, Q1, x);
+    uint32_t Q[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= 2 && !pairs) break;
+      const int o0 = pairs ? 2 * i : 4 * i, o1 = pairs ? 2 * i + 1 : 4 * i + 2;
+      const uint32_t a1[1] = {s_samp[o0][l]}, b1[1] = {s_samp[o1][l]};
+      wide_merge_full<1>(a1, b1, Q[i], x);
     }
     if constexpr (R == 2) {
-      P[0] = Q0[0];
-      P[1] = Q0[1];
-      wide_merge_top<2>(P, Q1, x);
+      P[0] = Q[0][0];
+      P[1] = Q[0][1];
+      wide_merge_top<2>(P, Q[1], x);
     } else {
-      wide_merge_full<2>(Q0, Q1, P, x);
+      wide_merge_full<2>(Q[0], Q[1], P, x);
+      if (pairs) {
+        uint32_t V[4];
+        wide_merge_full<2>(Q[2], Q[3], V, x);
+        wide_merge_top<4>(P, V, x);
+      }
     }
     const uint32_t te = wide_at<R>(P, a.k - 1);
     exact_floor = te > 0 ? te - 1 : 0;
-    if (a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks32 * kChunkVecs * kWave) {
+    if (speculate) {
       const uint32_t ts = wide_at<R>(P, a.spec_rank - 1);
       spec_floor = ts > 0 ? ts - 1 : 0;
     }
