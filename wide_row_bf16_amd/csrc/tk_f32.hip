@@ -778,9 +778,16 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan32_kernel(ArgmaxArgs32 
 // 64 < k <= 256 on fp32 rows: the multi-register scan of tk_wide.hip with the
 // 64-bit composites of this file -- each wave keeps 64 R composites (R = 2 or
 // 4 registers of 64 bits, tk_lists.h), filters on raw bits (Filter32), takes
-// the pooled exact and verified speculative floors, shares thresholds, merges
-// the four lists by rank in LDS, and folds split rows in their last
-// workgroup.
+// the pooled exact and verified speculative floors, collects candidates in
+// an LDS ring merged into the list 64 at a time (an insertion into four
+// 64-bit registers costs about fifty instructions: the ring took 1024 x
+// 151936 rows at k = 256 from 221-229 to 117-129 us), shares thresholds,
+// merges the four lists as a register tree, and folds split rows in their
+// last workgroup.
+
+// Pending candidates of a wave: a ring of 64-bit composites in LDS (a power
+// of two, above the 63 left after a batch plus the 256 one vector can add).
+constexpr int kWideRing32 = 512;
 
 template <int R>
 struct WaveWide32 {
@@ -791,6 +798,9 @@ struct WaveWide32 {
   uint32_t flags;
   int km1, qm1, wave;
   uint32_t *tau;
+  uint64_t *ring;  // LDS: this wave's kWideRing32 pending composites
+  uint32_t r0;     // wave-uniform ring index of the oldest pending composite
+  uint32_t nr;     // wave-uniform count of pending composites
   Xchg x;
 };
 
@@ -818,28 +828,59 @@ __device__ __forceinline__ void wide32_publish(const WaveWide32<R> &w) {
   }
 }
 
-// One vector of four elements per lane (lanes `lanes`), element by element
-// (a runtime loop rotating the words keeps one copy of the insertion code).
+// The oldest min(64, pending) candidates leave the ring as one batch, sorted
+// and cascaded into the list; the k-th and the published keys follow.
 template <int R>
-__device__ __forceinline__ void wide32_vector(WaveWide32<R> &w, uint4 d, uint32_t col0, uint64_t lanes) {
-#pragma unroll 1
-  for (int e = 0; e < kElems32; ++e) {
-    const uint32_t b = d.x;
-    d = make_uint4(d.y, d.z, d.w, d.x);
-    const uint32_t key = key32(b);
-    if (lanes & ballot(key == 0)) w.flags |= kNan;
-    if (lanes & ballot(b == 0xFF800000u)) w.flags |= kNinf;
-    const uint64_t c = key > w.ext ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e)) : 0;
-    const uint64_t m = lanes & lanes_ugt64(c, w.kth);
-    if (m) wide32_offer<R>(w, c, m);
-  }
+__device__ __forceinline__ void wide32_flush(WaveWide32<R> &w) {
+  __builtin_amdgcn_wave_barrier();  // the ring's stores above precede its loads
+  const uint32_t take = min(w.nr, (uint32_t)kWave);
+  const uint32_t l = (uint32_t)lane_id();
+  const uint64_t v = l < take ? w.ring[(w.r0 + l) & (kWideRing32 - 1)] : 0;
+  w.r0 = (w.r0 + take) & (kWideRing32 - 1);
+  w.nr -= take;
+  wide_merge_batch64<R>(w.L, v, w.x);
+  w.kth = wide_at64<R>(w.L, w.km1);
+  wide32_publish<R>(w);
 }
 
+// One vector of four elements per lane (lanes `lanes`): per element, the
+// lanes whose key exceeds t (the k-th's key at the last batch, or ext) append
+// their composites to the ring, and -inf / NaN patterns are flagged.  Every
+// vector of a chunk lies at higher columns than the entries the k-th came
+// from, so an equal key loses to it and the key test is exact; pending
+// composites only lag the k-th (extra candidates land at ranks >= k).
+template <int R>
+__device__ __forceinline__ void wide32_vector(WaveWide32<R> &w, uint4 d, uint32_t col0, uint64_t lanes, uint32_t t) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint64_t nan = 0, ninf = 0;
+#pragma unroll
+  for (int e = 0; e < kElems32; ++e) {
+    const uint32_t b = dw[e];
+    const uint32_t key = key32(b);
+    nan |= lanes & lanes_eq(key, 0u);
+    ninf |= lanes & lanes_eq(b, 0xFF800000u);
+    const uint64_t h = lanes & lanes_ugt(key, t);
+    if (h) {
+      const uint32_t slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(h >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)h, w.r0 + w.nr));
+      if (__builtin_amdgcn_inverse_ballot_w64(h))
+        w.ring[slot & (kWideRing32 - 1)] = ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e));
+      w.nr += (uint32_t)__popcll(h);
+    }
+  }
+  if (nan) w.flags |= kNan;
+  if (ninf) w.flags |= kNinf;
+}
+
+// One chunk: trips against the thresholds at its start, then the tripped
+// vectors in column order; every 64 pending candidates are merged into the
+// list as a batch, after which the key threshold is taken again.
 template <int R>
 __device__ __forceinline__ void wide32_chunk(WaveWide32<R> &w, const uint4 (&v)[kChunkVecs], uint32_t first,
                                              uint32_t nvec, uint32_t col_first) {
   w.ext = max(shared_bound32(w.tau, w.wave), w.floor);
-  const Filter32 f = filter32_for(max((uint32_t)(w.kth >> 32), w.ext), w.flags);
+  uint32_t t = max((uint32_t)(w.kth >> 32), w.ext);
+  const Filter32 f = filter32_for(t, w.flags);
   const uint32_t l = (uint32_t)lane_id();
   uint64_t trip[kChunkVecs], any = 0;
 #pragma unroll
@@ -853,7 +894,15 @@ __device__ __forceinline__ void wide32_chunk(WaveWide32<R> &w, const uint4 (&v)[
   uint32_t col = col_first + kElems32 * (first + l);
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
-    if (t0) wide32_vector<R>(w, x0, col, t0);
+    if (t0) {
+      wide32_vector<R>(w, x0, col, t0, t);
+      if (w.nr >= (uint32_t)kWave) {
+        do {
+          wide32_flush<R>(w);
+        } while (w.nr >= (uint32_t)kWave);
+        t = max((uint32_t)(w.kth >> 32), w.ext);
+      }
+    }
     x0 = x1;
     x1 = x2;
     x2 = x3;
@@ -864,7 +913,6 @@ __device__ __forceinline__ void wide32_chunk(WaveWide32<R> &w, const uint4 (&v)[
     if (!(t0 | t1 | t2)) break;
     col += kElems32 * kWave;
   }
-  wide32_publish<R>(w);
 }
 
 template <int R>
@@ -1007,6 +1055,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
   __shared__ uint32_t s_samp[2 * kWgWaves][kWave];
+  __shared__ uint64_t s_ring[kWgWaves][kWideRing32];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -1113,10 +1162,14 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
     w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
     w.wave = wave;
     w.tau = s_tau;
+    w.ring = s_ring[wave];
+    w.r0 = 0;
+    w.nr = 0;
     w.x = x;
 
     if (wave == 0 && head_hi > 0) wide32_columns<R>(w, row, 0, head_hi);
     if (wn > 0) wide32_body<R>(w, wvp, wn, (uint32_t)(a0 + kElems32 * wv0), A);
+    while (w.nr > 0) wide32_flush<R>(w);
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) wide32_columns<R>(w, row, tail_lo, tail_hi);
 
     int cnt = 0;

@@ -5,7 +5,8 @@
 // kernels' anonymous namespace (in namespace tk), after tk_wave.h.
 //  - One insertion applies the one-register rule max(entry, min(shifted, c))
 //    to every register at once, the shift being DPP wave_shr:1 with the
-//    previous register's lane 63 as lane 0's source.
+//    previous register's lane 63 as lane 0's source (the row edges' columns;
+//    the scans' chunks collect candidates in LDS and merge them as batches).
 //  - A sorted batch of 64 cascades down the registers: against register j,
 //    the lane-wise max of the register and the reversed batch is the top 64
 //    of both (a bitonic sequence, sorted in six stages) and stays; the

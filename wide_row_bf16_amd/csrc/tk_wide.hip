@@ -8,23 +8,26 @@
 //
 // Kept set.  A wave keeps its 64 R best composites in R VGPRs (R = 2 for
 // k <= 128, 4 for k <= 256): register j, lane i holds rank 64 j + i of the
-// concatenated descending list.
-//  - One insertion shifts every register right by one lane (DPP wave_shr),
-//    register j's lane 0 taking register j - 1's lane 63, and keeps
-//    max(entry, min(shifted, c)) -- the one-register rule applied to the
-//    whole list at once.
-//  - A batch of 64 is sorted and cascaded down the registers: against
-//    register j, the lane-wise max of the register and the reversed batch is
-//    the top 64 of both (a bitonic sequence, sorted in six stages) and stays;
-//    the lane-wise min, sorted likewise, is carried to register j + 1.
-//    Registers whose last entry already beats the batch's first are skipped.
+// concatenated descending list.  Candidates do not enter it one by one: the
+// lanes of one element position that pass the filter append their
+// composites to a ring in LDS (slots from mbcnt over the hit mask: about ten
+// instructions for the whole position, against about twenty per entry for
+// an insertion into four registers), and every 64 pending ones enter as one
+// batch, sorted and cascaded down the registers: against register j, the
+// lane-wise max of the register and the reversed batch is the top 64 of both
+// (a bitonic sequence, sorted in six stages) and stays; the lane-wise min,
+// sorted likewise, is carried to register j + 1.  Registers whose last entry
+// already beats the batch's first are skipped.  The k-th and the published
+// keys lag the pending candidates, which only lets extra ones through (the
+// k = 256 scan is bound by its VALU issue: on 1024 x 151936 rows the ring
+// took it from 79-84 to 67-73 us).
 // The filter, the trip masks, the chunk loads and the flags are those of the
 // k <= 64 scan.  The exact floor is the k-th largest of the 256 lane maxima
 // of each wave's first chunk (k lanes hold an element at or above it; on
 // few-row splits at k > 128, of each lane's two largest keys); a speculative
 // floor (a lower rank of the same sample, verified after the scan and
 // followed by a rescan under the exact floor when it fails) spares most of
-// the insertions on wide spans.  The four wave lists meet as a tree of
+// the candidates on wide spans.  The four wave lists meet as a tree of
 // bitonic list merges in registers; split rows are folded by their last
 // workgroup with the same 64-bit list merges.
 #include <hip/hip_runtime.h>
@@ -44,9 +47,9 @@ namespace {
 // A speculative floor is tried only when each wave's share spans at least this
 // many chunks (shorter shares are mostly sample already).
 constexpr int kWideSpecChunks = 4;
-// This many tripping lanes in a vector take the dense path (all composites,
-// a per-lane sort, batch merges); fewer take the per-element lean path.
-constexpr int kWideDenseLanes = 16;
+// Pending candidates of a wave: a ring in LDS (a power of two, above the 63
+// left after a batch plus the 512 one vector can add).
+constexpr int kWideRing = 1024;
 
 template <int R>
 struct WaveWide {
@@ -60,6 +63,9 @@ struct WaveWide {
   int qm1;         // ceil(k / 4) - 1 (< 64)
   int wave;
   uint32_t *tau;   // LDS: [k-th key of each wave][ceil(k/4)-th key of each wave]
+  uint32_t *ring;  // LDS: this wave's kWideRing pending composites
+  uint32_t r0;     // wave-uniform ring index of the oldest pending composite
+  uint32_t nr;     // wave-uniform count of pending composites
   Xchg x;
 };
 
@@ -107,13 +113,33 @@ __device__ __forceinline__ void wide_publish(WaveWide<R> &w) {
   }
 }
 
-// Few tripping lanes: the eight per-element tests against T on the raw bits
-// (lanes `valid`), then, for each element position with hits, the composites
-// of all lanes at once and one insertion per hit (the lean path of the k <= 64
-// scan).  NONNEG: T >= 0, so only non-negative bit patterns pass, with key =
-// bits + 0x8000; NaN patterns that pass are flagged, never kept.
+// The oldest min(64, pending) candidates leave the ring as one batch: sorted
+// and cascaded into the list (the top 64 R of both stay); the k-th and the
+// published keys follow the list.
+template <int R>
+__device__ __forceinline__ void wide_flush(WaveWide<R> &w) {
+  __builtin_amdgcn_wave_barrier();  // the ring's stores above precede its loads
+  const uint32_t take = min(w.nr, (uint32_t)kWave);
+  const uint32_t l = (uint32_t)lane_id();
+  const uint32_t v = l < take ? w.ring[(w.r0 + l) & (kWideRing - 1)] : 0u;
+  w.r0 = (w.r0 + take) & (kWideRing - 1);
+  w.nr -= take;
+  wide_merge_batch<R>(w.L, v, w.x);
+  w.kth = wide_at<R>(w.L, w.km1);
+  wide_publish<R>(w);
+}
+
+// The eight per-element tests of one tripped vector against T on the raw
+// bits (lanes `valid`); for each element position with hits, the composites
+// of the hitting lanes are appended to the ring (their slots counted by
+// mbcnt over the hit mask), whatever their number.  NONNEG: T >= 0, so only
+// non-negative bit patterns pass, with key = bits + 0x8000.  NaN patterns
+// that pass are flagged, never kept.  A composite that passes beats the k-th
+// of the list (its key exceeds the k-th's key); pending composites are not
+// in the list yet, so the k-th and the published keys lag, which only lets
+// extra candidates through (they land at ranks >= k).
 template <int R, bool NONNEG>
-__device__ __forceinline__ void wide_lanes_value(WaveWide<R> &w, uint4 d, uint32_t inv0, uint64_t valid,
+__device__ __forceinline__ void wide_take_vector(WaveWide<R> &w, uint4 d, uint32_t inv0, uint64_t valid,
                                                  const Filter &f) {
   const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
   uint64_t m[8];
@@ -123,28 +149,30 @@ __device__ __forceinline__ void wide_lanes_value(WaveWide<R> &w, uint4 d, uint32
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
     m[e] = (NONNEG ? lanes_sgt((int32_t)(int16_t)b, f.t16) : lanes_ult(b, f.tu)) & valid;
   }
+  uint64_t nan = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (!m[e]) continue;
     const uint32_t word = dw[e >> 1];
     const uint32_t b = (e & 1) ? word >> 16 : word & 0xFFFFu;
     const uint32_t key = NONNEG ? (b > w.inf ? 0u : b | 0x8000u) : order_key(b, w.inf);
-    if (m[e] & lanes_eq(key, 0u)) w.flags |= kNan;
-    const uint32_t c = key ? (key << 16) | (inv0 - (uint32_t)e) : 0u;
-    uint64_t h = m[e] & lanes_ugt(c, w.kth);
-    while (h) {  // against a stale k-th: extra entries land at ranks >= k only
-      const int l = __builtin_ctzll(h);
-      h &= h - 1;
-      wide_insert_one<R>(w.L, readlane(c, l));
+    const uint64_t h = m[e] & ~lanes_eq(key, 0u);
+    nan |= m[e] & ~h;
+    if (h) {
+      const uint32_t slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(h >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)h, w.r0 + w.nr));
+      if (__builtin_amdgcn_inverse_ballot_w64(h)) w.ring[slot & (kWideRing - 1)] = (key << 16) | (inv0 - (uint32_t)e);
+      w.nr += (uint32_t)__popcll(h);
     }
   }
-  w.kth = wide_at<R>(w.L, w.km1);
+  if (nan) w.flags |= kNan;
 }
 
 // One loaded chunk (vector u of this lane = the wave's vector first + 64 u +
 // lane): trip masks against T at the chunk start, then for each tripped
-// vector the lanes' composites above T, sorted per lane, offered position by
-// position.  Positive NaN patterns pass the value test and are flagged here.
+// vector the composites above T go to the ring; every 64 pending ones are
+// merged into the list as a batch, after which T is taken again.  Positive
+// NaN patterns pass the value test and are flagged here.
 template <int R>
 __device__ __forceinline__ void wide_chunk(WaveWide<R> &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                            int64_t col_first, int64_t base) {
@@ -167,37 +195,18 @@ __device__ __forceinline__ void wide_chunk(WaveWide<R> &w, const uint4 (&v)[kChu
   uint4 x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
   uint64_t m0 = vt[0], m1 = vt[1], m2 = vt[2], m3 = vt[3];
   uint32_t iv = 0xFFFFu - (uint32_t)(col_first - base) - (uint32_t)kVecElems * (first + l);
+  Filter f = f0;
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
-    if (m0 && __popcll(m0) < kWideDenseLanes) {
-      const Filter f = filter_for(max(w.kth >> 16, w.ext), w.flags, w.inf);
-      if (f.nonneg) wide_lanes_value<R, true>(w, x0, iv, m0, f);
-      else wide_lanes_value<R, false>(w, x0, iv, m0, f);
-    } else if (m0) {
-      const bool mine = (m0 >> l) & 1u;
-      const uint32_t t = max(w.kth >> 16, w.ext);
-      const uint32_t dw[4] = {x0.x, x0.y, x0.z, x0.w};
-      uint32_t c[8];
-      bool nan = false;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        const uint32_t key = order_key(b, w.inf);
-        nan |= mine && key == 0;
-        c[e] = (mine && key > t) ? (key << 16) | (iv - (uint32_t)e) : 0u;
+    if (m0) {
+      if (f.nonneg) wide_take_vector<R, true>(w, x0, iv, m0, f);
+      else wide_take_vector<R, false>(w, x0, iv, m0, f);
+      if (w.nr >= (uint32_t)kWave) {
+        do {
+          wide_flush<R>(w);
+        } while (w.nr >= (uint32_t)kWave);
+        f = filter_for(max(w.kth >> 16, w.ext), w.flags, w.inf);
       }
-      if (ballot(nan)) w.flags |= kNan;
-      sort8_desc(c);
-#pragma unroll 1
-      for (int p = 0; p < 8; ++p) {
-        const uint64_t m = lanes_ugt(c[0], w.kth);
-        if (!m) break;
-        wide_offer<R>(w, c[0], m);
-        c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = c[4]; c[4] = c[5]; c[5] = c[6]; c[6] = c[7]; c[7] = 0;
-      }
-      // the kept set just grew a lot: share it and take the others' news
-      wide_publish<R>(w);
-      w.ext = max(wide_bound(w.tau, w.wave), w.floor);
     }
     m0 = m1;
     m1 = m2;
@@ -209,7 +218,6 @@ __device__ __forceinline__ void wide_chunk(WaveWide<R> &w, const uint4 (&v)[kChu
     x2 = x3;
     iv -= (uint32_t)(kWave * kVecElems);
   }
-  wide_publish<R>(w);
 }
 
 // Columns [lo, hi) one per lane (row edges, tiny spans).
@@ -342,6 +350,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
   __shared__ uint32_t s_samp[2 * kWgWaves][kWave];
+  __shared__ uint32_t s_ring[kWgWaves][kWideRing];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -463,6 +472,9 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
     w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
     w.wave = wave;
     w.tau = s_tau;
+    w.ring = s_ring[wave];
+    w.r0 = 0;
+    w.nr = 0;
 
     if (wave == 0 && head_hi > 0) wide_columns<R>(w, row, 0, head_hi, base);
     if (wn > 0) {
@@ -487,6 +499,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
         wide_chunk<R>(w, B, first + kStep, wn, col_first, base);
       }
     }
+    while (w.nr > 0) wide_flush<R>(w);
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) wide_columns<R>(w, row, tail_lo, tail_hi, base);
     TK_WAVE_STAMP(2 + wave);
 
