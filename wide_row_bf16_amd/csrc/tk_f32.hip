@@ -18,7 +18,8 @@
 // priority falling with progress, the four wave lists meeting as a tree of
 // register merges, and the last workgroup of a split row folding the span
 // lists), with four fp32 elements per 16-byte vector and 64-bit list
-// entries.
+// entries.  Unlike the bf16 scan, candidates of the exact path collect in an
+// LDS ring and enter the list in sorted batches (kRing32Flush).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -88,8 +89,22 @@ struct Wave32 {
   uint32_t flags;  // wave-uniform NaN / -inf flags seen so far
   int km1, qm1, wave;
   uint32_t *tau;   // LDS: published k-th and ceil(k/4)-th keys of the waves
+  uint64_t *ring;  // LDS: this wave's kRing32 pending composites
+  uint32_t r0;     // wave-uniform ring index of the oldest pending composite
+  uint32_t nr;     // wave-uniform count of pending composites
   Xchg x;
 };
+
+// Candidates of the exact path wait in an LDS ring (a power of two, above
+// the 31 left after a merge plus the 256 one vector can add) and enter the
+// list as sorted batches once 32 are pending: appending costs about ten
+// instructions per element position, an insertion of one 64-bit entry about
+// twenty per entry.  On MI355X the ring took 1024 x 151936 fp32 rows at
+// k = 64 from 110-115 to 105-106 us, 16 x 248320 at k = 20 from 25.4 to
+// 21.2 us and 64 x 151936 at k = 16 from 29.3 to 25.4 us (batches at 64
+// pending: 106, 20.8, 27.1 us; at 16: 108, 21.7, 25.9 us).
+constexpr int kRing32 = 512;
+constexpr int kRing32Flush = 32;
 
 // Adds the candidates c of lanes m (and of no other lane): one bitonic batch
 // when many, else one insertion each (against a k-th refreshed only
@@ -154,11 +169,6 @@ __device__ __forceinline__ Filter32 filter32_for(uint32_t t, uint32_t flags) {
   return f;
 }
 
-__device__ __forceinline__ Filter32 make_filter32(const Wave32 &w) {
-  const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(w.kth >> 32));
-  const uint32_t t = max(own, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.ext));
-  return filter32_for(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)w.flags));
-}
 
 __device__ __forceinline__ uint64_t value_trip(uint4 d, const Filter32 &f) {
   if (f.nonneg) {
@@ -175,23 +185,43 @@ __device__ __forceinline__ uint64_t flag_trip(uint4 d, const Filter32 &f) {
   return lanes_uge(a, f.ftrip);
 }
 
-// Exact path for one vector of four elements per lane (lanes `lanes`):
-// per element, the composites of all lanes, then the lanes that beat the
-// k-th -- one insertion each, or one batch when many.
-__device__ __forceinline__ void take_vector32(Wave32 &w, uint4 d, uint32_t col0, uint64_t lanes) {
-  // one element position per iteration: a runtime loop (rotating the
-  // vector's words) keeps a single copy of the insertion code
-#pragma unroll 1
+// The oldest min(64, pending) candidates leave the ring as one batch, sorted
+// and merged into the list; the k-th and the published keys follow.
+__device__ __forceinline__ void flush32(Wave32 &w) {
+  __builtin_amdgcn_wave_barrier();  // the ring's stores above precede its loads
+  const uint32_t take = min(w.nr, (uint32_t)kWave);
+  const uint32_t l = (uint32_t)lane_id();
+  const uint64_t v = l < take ? w.ring[(w.r0 + l) & (kRing32 - 1)] : 0;
+  w.r0 = (w.r0 + take) & (kRing32 - 1);
+  w.nr -= take;
+  w.list = merge_sorted64(w.list, sort64_desc64(v, w.x), w.x);
+  w.kth = readlane64(w.list, w.km1);
+  publish32(w);
+}
+
+// Exact path for one vector of four elements per lane (lanes `lanes`): per
+// element, the lanes whose key exceeds t append their composites to the
+// ring (see wide32_vector), and -inf / NaN patterns are flagged.
+__device__ __forceinline__ void take_vector32(Wave32 &w, uint4 d, uint32_t col0, uint64_t lanes, uint32_t t) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  uint64_t nan = 0, ninf = 0;
+#pragma unroll
   for (int e = 0; e < kElems32; ++e) {
-    const uint32_t b = d.x;
-    d = make_uint4(d.y, d.z, d.w, d.x);
+    const uint32_t b = dw[e];
     const uint32_t key = key32(b);
-    if (lanes & ballot(key == 0)) w.flags |= kNan;
-    if (lanes & ballot(b == 0xFF800000u)) w.flags |= kNinf;
-    const uint64_t c = key > w.ext ? ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e)) : 0;
-    const uint64_t m = lanes & lanes_ugt64(c, w.kth);
-    if (m) offer64(w, c, m);
+    nan |= lanes & lanes_eq(key, 0u);
+    ninf |= lanes & lanes_eq(b, 0xFF800000u);
+    const uint64_t h = lanes & lanes_ugt(key, t);
+    if (h) {
+      const uint32_t slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(h >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)h, w.r0 + w.nr));
+      if (__builtin_amdgcn_inverse_ballot_w64(h))
+        w.ring[slot & (kRing32 - 1)] = ((uint64_t)key << 32) | (0xFFFFFFFFu - (col0 + (uint32_t)e));
+      w.nr += (uint32_t)__popcll(h);
+    }
   }
+  if (nan) w.flags |= kNan;
+  if (ninf) w.flags |= kNinf;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -251,7 +281,8 @@ __device__ __forceinline__ void lane_top2_keys32(const uint4 (&v)[kChunkVecs], u
 __device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
                                              uint32_t col_first) {
   w.ext = max(shared_bound32(w.tau, w.wave), w.floor);
-  const Filter32 f = make_filter32(w);
+  uint32_t t = max((uint32_t)(w.kth >> 32), w.ext);
+  const Filter32 f = filter32_for(t, w.flags);
   const uint32_t l = (uint32_t)lane_id();
   uint64_t any = 0, trip[kChunkVecs];
 #pragma unroll
@@ -265,7 +296,15 @@ __device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkV
   uint32_t col = col_first + kElems32 * (first + l);
 #pragma unroll 1
   for (int u = 0; u < kChunkVecs; ++u) {
-    if (t0) take_vector32(w, x0, col, t0);
+    if (t0) {
+      take_vector32(w, x0, col, t0, t);
+      if (w.nr >= (uint32_t)kRing32Flush) {
+        do {
+          flush32(w);
+        } while (w.nr >= (uint32_t)kRing32Flush);
+        t = max((uint32_t)(w.kth >> 32), w.ext);
+      }
+    }
     x0 = x1;
     x1 = x2;
     x2 = x3;
@@ -276,7 +315,6 @@ __device__ __forceinline__ void take_chunk32(Wave32 &w, const uint4 (&v)[kChunkV
     if (!(t0 | t1 | t2)) break;
     col += kElems32 * kWave;
   }
-  publish32(w);
 }
 
 // Streams nvec vectors from vp (element 0 is column col_first), two chunks in
@@ -421,6 +459,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
   __shared__ uint32_t s_flags[kWgWaves];
   __shared__ uint32_t s_tau[2 * kWgWaves];
   __shared__ uint32_t s_samp[kWgWaves][kWave];
+  __shared__ uint64_t s_ring[kWgWaves][kRing32];
 
   const int64_t blk = blockIdx.x;
   const int64_t r = a.row0 + blk / a.spans;
@@ -495,10 +534,14 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
     w.qm1 = (a.k + kWgWaves - 1) / kWgWaves - 1;
     w.wave = wave;
     w.tau = s_tau;
+    w.ring = s_ring[wave];
+    w.r0 = 0;
+    w.nr = 0;
     w.x = make_xchg();
 
     if (wave == 0 && head_hi > head_lo) take_columns32(w, row, head_lo, head_hi);
     if (wn > 0) take_body32(w, wvp, wn, (uint32_t)(a0 + kElems32 * wv0), A);
+    while (w.nr > 0) flush32(w);
     if (wave == kWgWaves - 1 && tail_hi > tail_lo) take_columns32(w, row, tail_lo, tail_hi);
 
     const uint64_t valid_mask = ballot(w.list != 0);
