@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
       a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
   {
     const Xchg x = make_xchg();
-    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key(A, 0, wn, a.inf) : 0u, x);
+    const uint32_t lm = wn == 0 ? 0u : S > 1 ? lane_max_key(A, 0, wn, a.inf) : lane_max_key_keys(A, 0, wn, a.inf);
+    s_samp[wave][l] = sort64_desc(lm, x);
     __syncthreads();
     uint32_t v[kWgWaves];  // pairwise tree of the sorted lists: the top 64 of all
 #pragma unroll
