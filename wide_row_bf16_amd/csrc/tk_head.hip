@@ -147,10 +147,11 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   // span.  Without it every wave of the grid reads the same block offset of
   // rows w_stride apart at the same time: requests that share their low
   // address bits and so crowd onto the same memory channels.  With one row
-  // tile (the memory-bound case) the rotation measured 117 -> 103 us on
-  // 15 x 2048 x 98592; with two or four row tiles it measured slower and is
-  // not used.  Only the order of the fp32 sums changes.
-  const int rot = RT == 1 ? (int)((((uint32_t)s * 2654435761u) >> 16) % (uint32_t)nblk) : 0;
+  // tile the rotation measured 117 -> 103 us on 15 x 2048 x 98592, with four
+  // (nontemporal loads) 154 -> 146 us on 64 rows; with two it measured
+  // slower (118 -> 122 us on 32 rows) and is not used.  Only the order of
+  // the fp32 sums changes.
+  const int rot = RT != 2 ? (int)((((uint32_t)s * 2654435761u) >> 16) % (uint32_t)nblk) : 0;
   auto phys = [&](int blk) {  // blocks past the last (loaded, never used) keep their index
     if (blk >= nblk) return blk;
     const int p = blk + rot;
@@ -170,14 +171,18 @@ __global__ __launch_bounds__(kHeadThreads, RT == 4 ? 2 : 1) void head_scan_kerne
   // Loads are unconditional (a branch around them makes the compiler wait for
   // every outstanding load at the join); the bytes of a block past `hidden`
   // -- the next row's, or zeros past the buffer's range -- are zeroed in
-  // registers, and blocks past the last are loaded but never used.
+  // registers, and blocks past the last are loaded but never used.  w is read
+  // once, so its loads take the scans' nontemporal policy: a plain read of
+  // these blocks (whole lines per request) streams at ~6.5 TB/s with it and
+  // ~5.7 without, and the head on 15 x 2048 x 98592 went from 94.7 to 84.0 us
+  // per call (32 rows 121.5 -> 113.7, 64 rows 155.5 -> 151.5).
   auto load_block = [&](HeadBlock &B, int logical) {
     const int blk = phys(logical);
     const bool in = (int64_t)blk * kHeadBlockBytes + lbyte < hidden_bytes;
 #pragma unroll
     for (int q = 0; q < kHeadBlockLoads; ++q) {
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, (int)(g_lane + q * g_q + (uint32_t)blk * kHeadBlockBytes), 0, 0);
+          rw, (int)(g_lane + q * g_q + (uint32_t)blk * kHeadBlockBytes), 0, kLoadPolicy);
       B.v[q] = in ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
