@@ -293,6 +293,29 @@ __device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t
   }
 }
 
+// A floor from the end of a wave's share, for rows that rise along it: there
+// every vector would beat the list before it and take the exact path.  The
+// k-th largest lane maximum of the share's last chunk is reached by k
+// elements of the share, so no key below it can be among the wave's k best
+// (equal keys pass: a lower column may win).  The chunk is read here for its
+// maxima only; its elements are taken in column order when the scan gets
+// there.  A wave asks for it when nearly every lane of its first chunk has its
+// largest key in its last vector (the lane's vectors lie 64 apart, so a rising
+// share puts every lane's maximum there; evenly spread data puts about a
+// quarter of them there).
+constexpr int kLookLanes = 56;       // lanes whose first-chunk maximum sits in their last vector
+constexpr uint32_t kLookChunks = 6;  // chunks in the wave's share for it to pay
+__device__ __forceinline__ uint32_t lookahead_floor(const uint4 *vp, uint32_t nvec, uint32_t lane_off, uint32_t inf,
+                                                int km1) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+  const uint32_t last = (nvec - 1) / kStep * kStep;
+  uint4 L[kChunkVecs];
+  load_chunk(L, vp, nvec, last, lane_off);
+  const uint32_t top = sort64_desc(lane_max_key(L, last, nvec, inf), make_xchg());
+  const uint32_t te = readlane(top, km1);
+  return te > 1 ? te - 1 : 0u;
+}
+
 // Fused merge of a split row.  Every scan workgroup of row r has written its
 // span list; the last one to arrive folds all S lists into the row's outputs,
 // with the order and rules of span_merge_kernel, and resets the row's counter
@@ -451,9 +474,9 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
   const bool speculate =
       a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
+  const uint32_t lm = wn == 0 ? 0u : S > 1 ? lane_max_key(A, 0, wn, a.inf) : lane_max_key_keys(A, 0, wn, a.inf);
   {
     const Xchg x = make_xchg();
-    const uint32_t lm = wn == 0 ? 0u : S > 1 ? lane_max_key(A, 0, wn, a.inf) : lane_max_key_keys(A, 0, wn, a.inf);
     s_samp[wave][l] = sort64_desc(lm, x);
     __syncthreads();
     uint32_t v[kWgWaves];  // pairwise tree of the sorted lists: the top 64 of all
@@ -470,6 +493,15 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     exact_floor = te > 0 ? te - 1 : 0;
     spec_floor = ts > 0 ? ts - 1 : 0;
   }
+  // rows that rise along this wave's share: a floor from its end (exact, so it
+  // also holds if the speculation fails)
+  uint32_t look_floor = 0;
+  if (wn >= kLookChunks * (uint32_t)(kChunkVecs * kWave)) {
+    const uint32_t l3 = vec_max_key(A[kChunkVecs - 1], a.inf);
+    if (__popcll(ballot(lm > 0 && l3 >= lm)) >= kLookLanes)
+      look_floor = lookahead_floor(wvp, wn, (uint32_t)l * 16u, a.inf, a.k - 1);
+  }
+  exact_floor = max(exact_floor, look_floor);
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {

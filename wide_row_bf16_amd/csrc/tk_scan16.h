@@ -158,6 +158,18 @@ __device__ __forceinline__ uint32_t lane_max_key(const uint4 (&v)[kChunkVecs], u
   return m >= 0 ? ((uint32_t)m > inf ? 0u : (uint32_t)m | 0x8000u) : order_key(n, inf);
 }
 
+// The largest order key of one vector of this lane, by the packed rule of
+// lane_max_key (never above the true maximum key).
+__device__ __forceinline__ uint32_t vec_max_key(uint4 v, uint32_t inf) {
+  const v2i16 smax = __builtin_elementwise_max(__builtin_elementwise_max(as_i16x2(v.x), as_i16x2(v.y)),
+                                               __builtin_elementwise_max(as_i16x2(v.z), as_i16x2(v.w)));
+  const v2u16 umin = __builtin_elementwise_min(__builtin_elementwise_min(as_u16x2(v.x), as_u16x2(v.y)),
+                                               __builtin_elementwise_min(as_u16x2(v.z), as_u16x2(v.w)));
+  const int32_t m = max((int32_t)smax.x, (int32_t)smax.y);
+  const uint32_t n = min((uint32_t)umin.x, (uint32_t)umin.y);
+  return m >= 0 ? ((uint32_t)m > inf ? 0u : (uint32_t)m | 0x8000u) : order_key(n, inf);
+}
+
 // The same lane maximum, key by key over the eight halves of each vector
 // (exact for lanes with NaN too).  The k <= 64 scan takes it for rows that
 // one workgroup scans whole: with the packed maximum the workgroups of
