@@ -103,3 +103,54 @@ def test_ascending_rows_fp16():
     x = upload(m)
     for k in KS:
         _check(m, cols, k, 1, "ascending fp16", fmt="f16", x=x)
+
+
+# The same floor in the k > 64 scans (from each lane's two or four largest
+# keys of the last chunk) and in the fp32 scans.
+WIDE_KS = [65, 128, 129, 200, 256]
+
+
+@pytest.mark.parametrize("cols", [98592, 151936])
+def test_ascending_rows_wide_k(cols):
+    m = family_rows("ascending", 3, cols, cols, seed=cols + 1)
+    x = upload(m)
+    for k in WIDE_KS:
+        for spans in (1, 0):
+            _check(m, cols, k, spans, "ascending wide", x=x)
+
+
+def test_rise_fall_and_plateau_wide_k():
+    cols = 151936
+    m = family_rows("ascending", 3, cols, cols, seed=23)
+    half = cols // 2
+    m[0, half:] = m[0, :cols - half][::-1]
+    m[1, cols // 3:] = m[1, -1]
+    x = upload(m)
+    for k in WIDE_KS:
+        _check(m, cols, k, 1, "rise-fall/plateau wide", x=x)
+
+
+def _check32(m, cols, k, spans, what, x):
+    want = oracle.topk_f32(m, cols, k)
+    log(f"rising f32 {what} cols={cols} k={k} spans={spans}")
+    assert_same(gpu_topk(m, cols, k, spans=spans, x=x, fmt="f32"), want, f"f32 {what} cols={cols} k={k} spans={spans}")
+
+
+@pytest.mark.parametrize("cols", [49152, 151936])
+def test_ascending_rows_fp32(cols):
+    m = family_rows("ascending", 3, cols, cols, seed=cols + 2, fmt="f32")
+    x = upload(m)
+    for k in KS + WIDE_KS:
+        for spans in (1, 0):
+            _check32(m, cols, k, spans, "ascending", x)
+
+
+def test_rise_fall_and_plateau_fp32():
+    cols = 151936
+    m = family_rows("ascending", 3, cols, cols, seed=29, fmt="f32")
+    half = cols // 2
+    m[0, half:] = m[0, :cols - half][::-1]
+    m[1, cols // 3:] = m[1, -1]
+    x = upload(m)
+    for k in (1, 32, 64, 128, 256):
+        _check32(m, cols, k, 1, "rise-fall/plateau", x)

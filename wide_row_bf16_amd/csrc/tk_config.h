@@ -31,6 +31,8 @@ constexpr int kBatchInsert = 8;                // >= this many new candidates: b
 constexpr int kSpecChunks = 16;                // chunks per wave before a speculative floor pays
 constexpr int kSampleElems = kWgWaves * kChunkVecs * kWave * kVecElems;  // pooled sample: each wave's first chunk
 constexpr double kSpecFailure = 1e-5;          // target probability that a speculative floor fails
+constexpr int kLookLanes = 56;                 // rising share: lanes whose first-chunk maximum sits in their last vector
+constexpr int kLookChunks = 6;                 // rising share: chunks of the wave's share for its end floor to pay
 constexpr int kHeadSpanCols = 256;             // vocabulary columns per workgroup of the fused head
 constexpr int kHeadMaxRows = 64;               // rows of the fused head: four 16-row matrix-core tiles
 constexpr size_t kFixedScratchBytes = size_t(2) << 20;  // scratch array of the allocation-free entry point

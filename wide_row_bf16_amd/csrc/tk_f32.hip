@@ -256,6 +256,54 @@ __device__ __forceinline__ uint32_t lane_max_key32(const uint4 (&v)[kChunkVecs],
   return m;
 }
 
+// This lane's R largest keys in a loaded chunk (vectors at or past nvec,
+// counted from the chunk's start, give none), in descending order: R
+// distinct elements.
+template <int R>
+__device__ __forceinline__ void lane_top_keys32(const uint4 (&v)[kChunkVecs], uint32_t nvec, uint32_t (&t)[R]) {
+#pragma unroll
+  for (int j = 0; j < R; ++j) t[j] = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const bool in = (uint32_t)(u * kWave + lane_id()) < nvec;
+    const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t key = in ? key32(e[i]) : 0u;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const uint32_t hi = max(t[j], key);
+        key = min(t[j], key);
+        t[j] = hi;
+      }
+    }
+  }
+}
+
+// A floor of the wave's own from the end of its share (its final 256
+// vectors), for rows that rise along it (the 16-bit scans describe the rule):
+// the k-th largest of each lane's R largest keys there, minus one; 0 for none.
+template <int R>
+__device__ __forceinline__ uint32_t rising_floor32(const uint4 *vp, uint32_t nvec, uint32_t lane_off, int k,
+                                                   const Xchg &x) {
+  constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+  const uint32_t last = nvec - kStep;  // the share's last kStep vectors: every lane holds four
+  uint4 L[kChunkVecs];
+  load_chunk32(L, vp, nvec, last, lane_off);
+  uint32_t t[R];
+  lane_top_keys32<R>(L, nvec - last, t);
+  const uint32_t te = rank_of_lane_keys<R>(t, k - 1, x);
+  return te > 1 ? te - 1 : 0u;
+}
+
+// Nearly every lane of the first chunk has its largest key in its last
+// vector: the wave's share rises (lanes' vectors lie 64 apart).
+__device__ __forceinline__ bool share_rises32(const uint4 (&A)[kChunkVecs], uint32_t lm) {
+  const uint4 v = A[kChunkVecs - 1];
+  const uint32_t l3 = max(max(key32(v.x), key32(v.y)), max(key32(v.z), key32(v.w)));
+  return __popcll(ballot(lm > 0 && l3 >= lm)) >= kLookLanes;
+}
+
 // This lane's two largest keys in a loaded chunk (*m2 = 0 with fewer than
 // two): distinct elements, for the deeper floor of few-row k > 128 splits.
 __device__ __forceinline__ void lane_top2_keys32(const uint4 (&v)[kChunkVecs], uint32_t nvec, uint32_t *m1,
@@ -495,9 +543,10 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
   if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
   const bool speculate = a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kSpecChunks * kChunkVecs * kWave;
   uint32_t exact_floor, spec_floor;
+  const uint32_t lm = wn > 0 ? lane_max_key32(A, wn) : 0u;
   {
     const Xchg x = make_xchg();
-    s_samp[wave][l] = sort64_desc(wn > 0 ? lane_max_key32(A, wn) : 0u, x);
+    s_samp[wave][l] = sort64_desc(lm, x);
     __syncthreads();
     uint32_t v[kWgWaves];
 #pragma unroll
@@ -512,6 +561,10 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
     exact_floor = te > 0 ? te - 1 : 0;
     spec_floor = ts > 0 ? ts - 1 : 0;
   }
+  // rows that rise along this wave's share: a floor of its own from the end
+  // (exact, so it also holds if the speculation fails)
+  if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) && share_rises32(A, lm))
+    exact_floor = max(exact_floor, rising_floor32<1>(wvp, wn, (uint32_t)l * 16u, a.k, make_xchg()));
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {
@@ -1139,8 +1192,9 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
   const bool speculate =
       a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks32 * kChunkVecs * kWave;
   const bool pairs = R == 4 && a.k > 2 * kWave && !speculate;
+  uint32_t m1 = 0;  // this lane's largest key of the first chunk
   {
-    uint32_t m1 = 0, m2 = 0;
+    uint32_t m2 = 0;
     if (wn > 0) {
       if (pairs) lane_top2_keys32(A, wn, &m1, &m2);
       else m1 = lane_max_key32(A, wn);
@@ -1182,6 +1236,10 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
       spec_floor = ts > 0 ? ts - 1 : 0;
     }
   }
+  // rows that rise along this wave's share: a floor of its own from the end,
+  // from each lane's R largest keys there (64 R distinct elements)
+  if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) && share_rises32(A, m1))
+    exact_floor = max(exact_floor, rising_floor32<R>(wvp, wn, (uint32_t)l * 16u, a.k, x));
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {

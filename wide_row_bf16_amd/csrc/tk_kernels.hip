@@ -295,20 +295,18 @@ __device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t
 
 // A floor from the end of a wave's share, for rows that rise along it: there
 // every vector would beat the list before it and take the exact path.  The
-// k-th largest lane maximum of the share's last chunk is reached by k
-// elements of the share, so no key below it can be among the wave's k best
-// (equal keys pass: a lower column may win).  The chunk is read here for its
-// maxima only; its elements are taken in column order when the scan gets
-// there.  A wave asks for it when nearly every lane of its first chunk has its
+// k-th largest lane maximum of the share's last chunk's worth of vectors (its
+// final 256, so that every lane holds four) is reached by k elements of the
+// share, so no key below it can be among the wave's k best (equal keys pass:
+// a lower column may win).  Those vectors are read here for their maxima
+// only; their elements are taken in column order when the scan gets there.  A wave asks for it when nearly every lane of its first chunk has its
 // largest key in its last vector (the lane's vectors lie 64 apart, so a rising
 // share puts every lane's maximum there; evenly spread data puts about a
 // quarter of them there).
-constexpr int kLookLanes = 56;       // lanes whose first-chunk maximum sits in their last vector
-constexpr uint32_t kLookChunks = 6;  // chunks in the wave's share for it to pay
 __device__ __forceinline__ uint32_t lookahead_floor(const uint4 *vp, uint32_t nvec, uint32_t lane_off, uint32_t inf,
                                                 int km1) {
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
-  const uint32_t last = (nvec - 1) / kStep * kStep;
+  const uint32_t last = nvec - kStep;  // the share's last kStep vectors: every lane holds four
   uint4 L[kChunkVecs];
   load_chunk(L, vp, nvec, last, lane_off);
   const uint32_t top = sort64_desc(lane_max_key(L, last, nvec, inf), make_xchg());
@@ -496,7 +494,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
   // rows that rise along this wave's share: a floor from its end (exact, so it
   // also holds if the speculation fails)
   uint32_t look_floor = 0;
-  if (wn >= kLookChunks * (uint32_t)(kChunkVecs * kWave)) {
+  if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave)) {
     const uint32_t l3 = vec_max_key(A[kChunkVecs - 1], a.inf);
     if (__popcll(ballot(lm > 0 && l3 >= lm)) >= kLookLanes)
       look_floor = lookahead_floor(wvp, wn, (uint32_t)l * 16u, a.inf, a.k - 1);

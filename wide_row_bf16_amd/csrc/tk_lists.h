@@ -106,6 +106,30 @@ __device__ __forceinline__ uint32_t wide_at(const uint32_t (&L)[R], int rank) {
   return v;
 }
 
+// The key of rank `rank` (0 = largest) among R keys per lane (each lane's
+// keys in descending order): every register sorted across the wave, then the
+// sorted lists merged.
+template <int R>
+__device__ __forceinline__ uint32_t rank_of_lane_keys(const uint32_t (&t)[R], int rank, const Xchg &x) {
+  static_assert(R == 1 || R == 2 || R == 4, "one, two or four keys per lane");
+  if constexpr (R == 1) {
+    return readlane(sort64_desc(t[0], x), rank);
+  } else if constexpr (R == 2) {
+    const uint32_t a[1] = {sort64_desc(t[0], x)}, b[1] = {sort64_desc(t[1], x)};
+    uint32_t Q[2];
+    wide_merge_full<1>(a, b, Q, x);
+    return wide_at<2>(Q, rank);
+  } else {
+    const uint32_t a0[1] = {sort64_desc(t[0], x)}, b0[1] = {sort64_desc(t[1], x)};
+    const uint32_t a1[1] = {sort64_desc(t[2], x)}, b1[1] = {sort64_desc(t[3], x)};
+    uint32_t Q0[2], Q1[2], P[4];
+    wide_merge_full<1>(a0, b0, Q0, x);
+    wide_merge_full<1>(a1, b1, Q1, x);
+    wide_merge_full<2>(Q0, Q1, P, x);
+    return wide_at<4>(P, rank);
+  }
+}
+
 // ---- 64-bit entries ----
 
 __device__ __forceinline__ uint64_t bitonic_merge64_u64(uint64_t v, const Xchg &x) {

@@ -170,6 +170,30 @@ __device__ __forceinline__ uint32_t vec_max_key(uint4 v, uint32_t inf) {
   return m >= 0 ? ((uint32_t)m > inf ? 0u : (uint32_t)m | 0x8000u) : order_key(n, inf);
 }
 
+// This lane's R largest keys in a loaded chunk, in descending order (zeros
+// for missing ones): R distinct elements.
+template <int R>
+__device__ __forceinline__ void lane_top_keys(const uint4 (&v)[kChunkVecs], uint32_t first, uint32_t nvec,
+                                              uint32_t inf, uint32_t (&t)[R]) {
+#pragma unroll
+  for (int j = 0; j < R; ++j) t[j] = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkVecs; ++u) {
+    const uint32_t dw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    const bool in = first + (uint32_t)(u * kWave + lane_id()) < nvec;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t key = in ? order_key((dw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu, inf) : 0u;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const uint32_t hi = max(t[j], key);
+        key = min(t[j], key);
+        t[j] = hi;
+      }
+    }
+  }
+}
+
 // The same lane maximum, key by key over the eight halves of each vector
 // (exact for lanes with NaN too).  The k <= 64 scan takes it for rows that
 // one workgroup scans whole: with the packed maximum the workgroups of

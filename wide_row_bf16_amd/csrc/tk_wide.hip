@@ -405,8 +405,9 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   const bool speculate =
       a.spec_rank > 0 && !a.exact && n / kWgWaves >= (int64_t)kWideSpecChunks * kChunkVecs * kWave;
   const bool pairs = R == 4 && a.k > 2 * kWave && !speculate;
+  uint32_t m1 = 0;  // this lane's largest key of the first chunk
   {
-    uint32_t m1 = 0, m2 = 0;
+    uint32_t m2 = 0;
     if (wn > 0) {
       if (pairs) lane_top2_keys(A, 0, wn, a.inf, &m1, &m2);
       else m1 = lane_max_key(A, 0, wn, a.inf);
@@ -447,6 +448,22 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       const uint32_t ts = wide_at<R>(P, a.spec_rank - 1);
       spec_floor = ts > 0 ? ts - 1 : 0;
     }
+  }
+  // Rows that rise along this wave's share (nearly every lane's first-chunk
+  // maximum in its last vector): a floor of its own from the share's final
+  // 256 vectors, as in the k <= 64 scan, from each lane's R largest keys there
+  // (64 R distinct elements, so the k-th exists); exact, so it also holds if
+  // the speculation fails.
+  if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) &&
+      __popcll(ballot(m1 > 0 && vec_max_key(A[kChunkVecs - 1], a.inf) >= m1)) >= kLookLanes) {
+    constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
+    const uint32_t last = wn - kStep;  // the share's last kStep vectors: every lane holds four
+    uint4 L[kChunkVecs];
+    load_chunk(L, wvp, wn, last, (uint32_t)l * 16u);
+    uint32_t t[R];
+    lane_top_keys<R>(L, last, wn, a.inf, t);
+    const uint32_t te = rank_of_lane_keys<R>(t, a.k - 1, x);
+    if (te > 1) exact_floor = max(exact_floor, te - 1);
   }
   uint32_t floor = exact_floor;
   bool verify = false;
