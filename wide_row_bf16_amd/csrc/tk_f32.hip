@@ -562,15 +562,18 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
     spec_floor = ts > 0 ? ts - 1 : 0;
   }
   // rows that rise along this wave's share: a floor of its own from the end
-  // (exact, so it also holds if the speculation fails)
+  // (exact, so it also holds if the speculation fails; the choice to
+  // speculate stays the same in every wave)
+  uint32_t rise_floor = 0;
   if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) && share_rises32(A, lm))
-    exact_floor = max(exact_floor, rising_floor32<1>(wvp, wn, (uint32_t)l * 16u, a.k, make_xchg()));
+    rise_floor = rising_floor32<1>(wvp, wn, (uint32_t)l * 16u, a.k, make_xchg());
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {
     floor = spec_floor;
     verify = true;
   }
+  floor = max(floor, rise_floor);
 
   int total = 0;
   uint32_t flags = 0;
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan32_kernel(ScanArgs32 a) {
       flags |= s_flags[o];
     }
     if (!verify || total >= a.k) break;  // exact, or the speculation verified
-    floor = exact_floor;                 // too few entries reach the speculative floor
+    floor = max(exact_floor, rise_floor);  // too few entries reach the speculative floor
     verify = false;
     if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
     __syncthreads();
@@ -1237,15 +1240,18 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
     }
   }
   // rows that rise along this wave's share: a floor of its own from the end,
-  // from each lane's R largest keys there (64 R distinct elements)
+  // from each lane's R largest keys there (64 R distinct elements); the
+  // choice to speculate stays the same in every wave
+  uint32_t rise_floor = 0;
   if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) && share_rises32(A, m1))
-    exact_floor = max(exact_floor, rising_floor32<R>(wvp, wn, (uint32_t)l * 16u, a.k, x));
+    rise_floor = rising_floor32<R>(wvp, wn, (uint32_t)l * 16u, a.k, x);
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {
     floor = spec_floor;
     verify = true;
   }
+  floor = max(floor, rise_floor);
 
   WaveWide32<R> w;
   int total = 0;
@@ -1292,7 +1298,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan32_kernel(ScanArgs32 a) {
       flags |= s_flags[o];
     }
     if (!verify || total >= a.k) break;  // exact, or the speculation verified
-    floor = exact_floor;
+    floor = max(exact_floor, rise_floor);
     verify = false;
     if (wn > 0) load_chunk32(A, wvp, wn, 0, (uint32_t)l * 16u);
     __syncthreads();

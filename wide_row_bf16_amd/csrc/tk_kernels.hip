@@ -491,21 +491,23 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     exact_floor = te > 0 ? te - 1 : 0;
     spec_floor = ts > 0 ? ts - 1 : 0;
   }
-  // rows that rise along this wave's share: a floor from its end (exact, so it
-  // also holds if the speculation fails)
-  uint32_t look_floor = 0;
+  // Rows that rise along this wave's share: a floor of the wave's own from the
+  // share's end.  It is exact, so it also holds when the speculation fails;
+  // the choice to speculate (and so the rescan loop below) stays the same in
+  // every wave of the workgroup.
+  uint32_t rise_floor = 0;
   if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave)) {
     const uint32_t l3 = vec_max_key(A[kChunkVecs - 1], a.inf);
     if (__popcll(ballot(lm > 0 && l3 >= lm)) >= kLookLanes)
-      look_floor = lookahead_floor(wvp, wn, (uint32_t)l * 16u, a.inf, a.k - 1);
+      rise_floor = lookahead_floor(wvp, wn, (uint32_t)l * 16u, a.inf, a.k - 1);
   }
-  exact_floor = max(exact_floor, look_floor);
   uint32_t floor = exact_floor;
   bool verify = false;
   if (spec_floor > exact_floor) {
     floor = spec_floor;
     verify = true;
   }
+  floor = max(floor, rise_floor);
   TK_STAMP(1);
 
   int total = 0;
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(kWgThreads) void span_scan_kernel(ScanArgs a) {
     }
     if (!verify || total >= a.k) break;  // exact, or the speculation verified
     // too few entries reach the speculative floor: scan again under the exact one
-    floor = exact_floor;
+    floor = max(exact_floor, rise_floor);
     verify = false;
     if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
     __syncthreads();  // every wave has read the counts above

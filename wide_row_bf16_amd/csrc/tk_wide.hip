@@ -453,7 +453,9 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
   // maximum in its last vector): a floor of its own from the share's final
   // 256 vectors, as in the k <= 64 scan, from each lane's R largest keys there
   // (64 R distinct elements, so the k-th exists); exact, so it also holds if
-  // the speculation fails.
+  // the speculation fails.  The choice to speculate stays the same in every
+  // wave of the workgroup.
+  uint32_t rise_floor = 0;
   if (wn >= (uint32_t)(kLookChunks * kChunkVecs * kWave) &&
       __popcll(ballot(m1 > 0 && vec_max_key(A[kChunkVecs - 1], a.inf) >= m1)) >= kLookLanes) {
     constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
     uint32_t t[R];
     lane_top_keys<R>(L, last, wn, a.inf, t);
     const uint32_t te = rank_of_lane_keys<R>(t, a.k - 1, x);
-    if (te > 1) exact_floor = max(exact_floor, te - 1);
+    if (te > 1) rise_floor = te - 1;
   }
   uint32_t floor = exact_floor;
   bool verify = false;
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
     floor = spec_floor;
     verify = true;
   }
+  floor = max(floor, rise_floor);
   TK_STAMP(1);
 
   WaveWide<R> w;
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(kWgThreads) void wide_scan_kernel(ScanArgs a) {
       flags |= s_flags[o];
     }
     if (!verify || total >= a.k) break;  // exact, or the speculation verified
-    floor = exact_floor;
+    floor = max(exact_floor, rise_floor);
     verify = false;
     if (wn > 0) load_chunk(A, wvp, wn, 0, (uint32_t)l * 16u);
     __syncthreads();  // every wave has read the counts above
