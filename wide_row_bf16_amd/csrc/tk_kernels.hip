@@ -299,12 +299,13 @@ __device__ __forceinline__ void take_body(WaveTopK &w, const uint4 *vp, uint32_t
 // final 256, so that every lane holds four) is reached by k elements of the
 // share, so no key below it can be among the wave's k best (equal keys pass:
 // a lower column may win).  Those vectors are read here for their maxima
-// only; their elements are taken in column order when the scan gets there.  A wave asks for it when nearly every lane of its first chunk has its
-// largest key in its last vector (the lane's vectors lie 64 apart, so a rising
+// only; their elements are taken in column order when the scan gets there.
+// A wave asks for it when nearly every lane of its first chunk has its
+// largest key in its last vector (a lane's vectors lie 64 apart, so a rising
 // share puts every lane's maximum there; evenly spread data puts about a
 // quarter of them there).
 __device__ __forceinline__ uint32_t lookahead_floor(const uint4 *vp, uint32_t nvec, uint32_t lane_off, uint32_t inf,
-                                                int km1) {
+                                                    int km1) {
   constexpr uint32_t kStep = (uint32_t)kChunkVecs * kWave;
   const uint32_t last = nvec - kStep;  // the share's last kStep vectors: every lane holds four
   uint4 L[kChunkVecs];
