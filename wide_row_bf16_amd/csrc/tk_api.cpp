@@ -575,6 +575,11 @@ int64_t plan_head(int64_t rows, int64_t vocab, int32_t cus) {
   return (int64_t)cus * ((ntiles + kTiles * cus - 1) / (kTiles * cus));
 }
 
+// Lists one merge workgroup of the fused head folds at a level of n lists per
+// row: all of them when they fit one workgroup, else groups of a quarter of
+// kMergeGroup (four-wave workgroups; the last level then folds the groups).
+int64_t head_group(int64_t n) { return n <= kMergeGroup ? n : kMergeGroup / 4; }
+
 // Fused head: the head kernel writes one candidate list per (row, span);
 // span_merge_kernel levels (groups of up to kMergeGroup lists, at least one
 // level) fold them into the outputs.
@@ -591,7 +596,7 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
   int64_t n = spans;
   do {
     level_lists[levels++] = n;
-    n = (n + kMergeGroup - 1) / kMergeGroup;
+    n = (n + head_group(n) - 1) / head_group(n);
   } while (n > 1);
   size_t off_list[8], off_count[8], off_flags[8], total = 0;
   for (int i = 0; i < levels; ++i) {
@@ -639,7 +644,7 @@ tk_status run_head(int64_t rows, int64_t hidden, int64_t vocab, int32_t k, const
     m.row0 = 0;
     m.k = k;
     m.lists_in = (int32_t)level_lists[i];
-    m.group = m.lists_in < kMergeGroup ? m.lists_in : kMergeGroup;
+    m.group = (int32_t)head_group(m.lists_in);
     m.lists_out = (m.lists_in + m.group - 1) / m.group;
     m.list_in = (const uint64_t *)(base + off_list[i]);
     m.count_in = (const int32_t *)(base + off_count[i]);

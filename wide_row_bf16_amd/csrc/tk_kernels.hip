@@ -832,10 +832,14 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan_kernel(ArgmaxArgs a) {
 // entry j; every load in flight at once) and folds them pairwise with bitonic
 // merges of the 64-bit composites -- the same (score desc, column asc) order
 // as the scan; the waves' results then meet in a tree through LDS.
-__global__ __launch_bounds__(kMergeThreads) void span_merge_kernel(MergeArgs a) {
-  constexpr int kWaves = kMergeThreads / kWave;
-  constexpr int kPerWave = kMergeGroup / kWaves;  // lists one wave folds
-  static_assert(kMergeGroup % kWaves == 0, "lists per wave");
+// WAVES = 16 folds up to kMergeGroup lists, WAVES = 4 up to a quarter of that
+// (four lists per wave either way; launch_span_merge picks the smaller
+// workgroup for small groups).
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void span_merge_kernel(MergeArgs a) {
+  constexpr int kWaves = WAVES;
+  constexpr int kPerWave = kMergeGroup / (kMergeThreads / kWave);  // lists one wave folds
+  static_assert(kMergeGroup % (kMergeThreads / kWave) == 0, "lists per wave");
   __shared__ uint64_t s_acc[kWaves][kWave];
   __shared__ int32_t s_cnt[kWaves];
   __shared__ uint32_t s_fl[kWaves];
@@ -1113,7 +1117,12 @@ hipError_t launch_argmax(const ArgmaxArgs &a, int64_t rows_in_launch, hipStream_
 
 hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStream_t stream) {
   const int64_t blocks = rows_in_launch * a.lists_out;
-  hipLaunchKernelGGL(span_merge_kernel, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, a);
+  constexpr int kPerWave = kMergeGroup / (kMergeThreads / kWave);
+  if (a.group <= 4 * kPerWave)
+    hipLaunchKernelGGL(span_merge_kernel<4>, dim3((uint32_t)blocks), dim3(4 * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL(span_merge_kernel<kMergeThreads / kWave>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
