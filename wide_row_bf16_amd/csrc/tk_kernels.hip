@@ -832,11 +832,12 @@ __global__ __launch_bounds__(kWgThreads) void argmax_scan_kernel(ArgmaxArgs a) {
 // entry j; every load in flight at once) and folds them pairwise with bitonic
 // merges of the 64-bit composites -- the same (score desc, column asc) order
 // as the scan; the waves' results then meet in a tree through LDS.
-// WAVES = 16 folds up to kMergeGroup lists, WAVES = 4 up to a quarter of that
-// (four lists per wave either way; launch_span_merge picks the smaller
-// workgroup for small groups).
+// WAVES = 16 folds up to kMergeGroup lists, WAVES = 8 or 4 up to a half or a
+// quarter of that (four lists per wave; launch_span_merge picks the smallest
+// workgroup that holds the group).  WAVES is a power of two for the tree.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void span_merge_kernel(MergeArgs a) {
+  static_assert((WAVES & (WAVES - 1)) == 0, "the waves' tree pairs wave i with i + w");
   constexpr int kWaves = WAVES;
   constexpr int kPerWave = kMergeGroup / (kMergeThreads / kWave);  // lists one wave folds
   static_assert(kMergeGroup % (kMergeThreads / kWave) == 0, "lists per wave");
@@ -1120,6 +1121,8 @@ hipError_t launch_span_merge(const MergeArgs &a, int64_t rows_in_launch, hipStre
   constexpr int kPerWave = kMergeGroup / (kMergeThreads / kWave);
   if (a.group <= 4 * kPerWave)
     hipLaunchKernelGGL(span_merge_kernel<4>, dim3((uint32_t)blocks), dim3(4 * kWave), 0, stream, a);
+  else if (a.group <= 8 * kPerWave)
+    hipLaunchKernelGGL(span_merge_kernel<8>, dim3((uint32_t)blocks), dim3(8 * kWave), 0, stream, a);
   else
     hipLaunchKernelGGL(span_merge_kernel<kMergeThreads / kWave>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0,
                        stream, a);
