@@ -202,8 +202,9 @@ tk_status tk_validate_bf16(int64_t rows, int64_t cols, int64_t row_stride, int32
 /*
  * The span count the automatic plan picks for a shape on a GPU with
  * `compute_units` CUs (host-only arithmetic; no HIP call).  For k == 1 that
- * is the plan of the argmax scan, for k > 64 that of the multi-register scan
- * (bf16 and fp16 rows).
+ * is the plan of the argmax scan, for k > 64 that of the multi-register scan,
+ * for 2 <= k <= 32 on few rows one of 8 to 12 spans by the row's width (bf16
+ * and fp16 rows).
  */
 int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_units);
 

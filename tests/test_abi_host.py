@@ -117,6 +117,13 @@ def test_plan():
     assert tk.plan_spans(1, 4096, 8) == 1            # too narrow to split
     assert tk.plan_spans(4, 10**7, 8) >= (10**7 // 8 + 32639) // 32640  # span width limit
     assert tk.plan_spans(100000, 10**6, 8) >= 4
+    # few rows, k <= 32: spans of about 12288 columns, 8 to 12 of them
+    assert tk.plan_spans(15, 98592, 32) == 8
+    assert tk.plan_spans(15, 49152, 32) == 8
+    assert tk.plan_spans(15, 151936, 32) == 12
+    assert tk.plan_spans(16, 248320, 20) == 12
+    assert tk.plan_spans(64, 151936, 16) == 4        # the CU count asks for fewer
+    assert tk.plan_spans(15, 98592, 64) == 12        # k = 64 keeps 12
     for rows in (1, 3, 15, 64, 255, 256, 1000):
         for cols in (0, 1, 4095, 4096, 70000, 151936, 248320, 600000):
             s = tk.plan_spans(rows, cols, 16)

@@ -60,7 +60,7 @@ def _both(m, cols, k, what, oracle_too=False):
 
 CASES = [
     # (first call, second call: smaller), each (family or config, rows, cols, stride, k)
-    (("c2", 15, 98592, 98592, 32), ("mixed_nonfinite", 3, 20000, 20003, 20)),   # fused folds, S = 12 then 4
+    (("c2", 15, 98592, 98592, 32), ("mixed_nonfinite", 3, 20000, 20003, 20)),   # fused folds, S = 8 then 4
     (("normal", 15, 98592, 98592, 1), ("logit", 4, 40000, 40000, 1)),            # argmax span slots
     # k > 64 with 62 spans a row (the span width limit): 17 rows need 2.16 MB of lists, so two row batches
     (("normal", 17, 16_000_000, 16_000_000, 256), ("normal", 15, 98592, 98592, 128)),

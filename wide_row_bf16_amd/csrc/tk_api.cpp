@@ -195,6 +195,32 @@ int32_t plan(int64_t rows, int64_t cols, int32_t compute_units) {
   return (int32_t)s;
 }
 
+// The 16-bit scan with k <= 32 on few rows: spans aimed at about
+// kNarrowSpanCols columns (a wave's share of about one and a half chunks),
+// but no fewer than kMinNarrowSpans.  Below 12 spans the row's fold chains
+// fewer merges, and at these k the longer shares cost less than that saves;
+// at k = 64 a wave's exact path is longer and 12 spans stay faster.  Measured
+// per call, forced span counts in alternated rounds on one box: 15 x 98592,
+// k = 32: 13.07 us at 8 spans against 13.43 at 12; 15 x 49152 and
+// 15 x 65536: 11.1 and 11.2 us at 8 against 11.9 and 12.2 at 12;
+// 15 x 151936 and 16 x 248320 keep 12 (14.05 and 17.3 us; 8 spans 14.6 and
+// 18.3); 15 x 98592 at k = 64: 13.8 us at 12 against 14.1 at 8.
+constexpr int64_t kNarrowSpanCols = 12288;
+constexpr int64_t kMinNarrowSpans = 8;
+constexpr int32_t kNarrowMaxK = 32;
+
+int32_t plan_scan16(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
+  int64_t s = plan(rows, cols, compute_units);
+  if (k <= kNarrowMaxK && s > kMinNarrowSpans) {
+    int64_t t = cols / kNarrowSpanCols;
+    if (t < kMinNarrowSpans) t = kMinNarrowSpans;
+    if (s > t) s = t;
+    const int64_t need = min_spans(cols);
+    if (s < need) s = need;
+  }
+  return (int32_t)s;
+}
+
 // Rank j of the speculative floor in a workgroup's pooled sample (the first
 // chunk of each wave).  The floor T is the sample's j-th largest lane
 // maximum, at most its j-th largest element; it fails (fewer than k keys of
@@ -715,7 +741,7 @@ tk_status run(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uint1
       return run_argmax(rows, cols, stride, in, out_idx, out_val, out_count, out_nonfinite, place, s1,
                         col_base, inf);
   }
-  const int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
+  const int32_t spans = forced > 0 ? forced : plan_scan16(rows, cols, k, device_cus(dev));
 
   tk::ScanArgs sa{};
   sa.in = in;
@@ -1153,7 +1179,7 @@ int32_t tk_plan_spans(int64_t rows, int64_t cols, int32_t k, int32_t compute_uni
     const int32_t s1 = plan_argmax(rows, cols, cus);
     if (s1 <= kMergeGroup) return s1;
   }
-  return plan(rows, cols, cus);
+  return plan_scan16(rows, cols, k, cus);
 }
 
 tk_status tk_probe_read(const void *in, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream) {
