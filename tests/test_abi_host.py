@@ -124,6 +124,13 @@ def test_plan():
     assert tk.plan_spans(16, 248320, 20) == 12
     assert tk.plan_spans(64, 151936, 16) == 4        # the CU count asks for fewer
     assert tk.plan_spans(15, 98592, 64) == 12        # k = 64 keeps 12
+    # 86 to 255 rows: twice the spans the CU count asks for (two or more workgroups per CU)
+    assert tk.plan_spans(96, 98592, 32) == 6
+    assert tk.plan_spans(128, 151936, 64) == 4
+    assert tk.plan_spans(255, 98592, 8) == 4
+    assert tk.plan_spans(128, 8192, 32) == 2         # no narrower than 4096 columns
+    assert tk.plan_spans(128, 12288, 32) == 3
+    assert tk.plan_spans(256, 151936, 64) == 1
     for rows in (1, 3, 15, 64, 255, 256, 1000):
         for cols in (0, 1, 4095, 4096, 70000, 151936, 248320, 600000):
             s = tk.plan_spans(rows, cols, 16)

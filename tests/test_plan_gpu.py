@@ -1,0 +1,37 @@
+"""The automatic plan on 86 to 255 rows, where the 16-bit scan takes twice the
+spans the CU count asks for, and on few rows at k <= 32, where it takes 8 to
+12 spans by the row's width: parity with the oracle, byte for byte, on the
+shapes that pick each branch (and a row width that caps the doubling)."""
+
+import pytest
+
+import oracle
+import wide_row_bf16_amd as tk
+from gpu_util import assert_same, gpu_topk, log, need_gpu
+from synth import family_rows
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # rows, cols, k, family
+    (96, 98592, 32, "normal"),
+    (128, 151936, 64, "normal"),
+    (200, 20000, 16, "few_levels"),
+    (255, 9000, 8, "nan_sprinkled"),
+    (128, 12288, 32, "normal"),        # doubling capped by the 4096-column span floor
+    (15, 49152, 32, "normal"),         # 8 spans at k <= 32
+    (15, 151936, 20, "neginf_one_finite"),
+    (15, 98592, 64, "normal"),         # k = 64 keeps 12
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("rows,cols,k,family", CASES)
+def test_automatic_plan_parity(rows, cols, k, family):
+    m = family_rows(family, rows, cols, cols + 8, seed=rows * 31 + k)
+    log(f"plan parity {rows}x{cols} k={k} {family} spans={tk.plan_spans(rows, cols, k)}")
+    assert_same(gpu_topk(m, cols, k, spans=0), oracle.topk_bf16(m, cols, k), f"{rows}x{cols} k={k} {family}")

@@ -208,9 +208,23 @@ int32_t plan(int64_t rows, int64_t cols, int32_t compute_units) {
 constexpr int64_t kNarrowSpanCols = 12288;
 constexpr int64_t kMinNarrowSpans = 8;
 constexpr int32_t kNarrowMaxK = 32;
+// Where the CU count asks for at most kDoubleMaxSpans spans (a third of the
+// CU count of rows or more, but fewer rows than CUs), the 16-bit scan takes
+// twice that many: two or more workgroups per CU, so one workgroup's fixed
+// chain (first load, floors, merges, fold) runs while another streams.
+// Measured per call, alternated rounds on one box (N(0, 2) rows): 96 x 98592
+// 16.6 us at 6 spans against 19.4 at 3; 128 x 98592 17.6 against 21.5;
+// 128 x 151936 at k = 64 23.4 against 30.3; 192 x 98592 19.3 against 22.8;
+// 224 x 98592 20.9 against 23.1.  At 64 rows (4 spans) doubling gained on
+// such rows but lost 0.4 us on rows of mixed ties and non-finite values.
+constexpr int64_t kDoubleMaxSpans = 3;
 
 int32_t plan_scan16(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
   int64_t s = plan(rows, cols, compute_units);
+  if (rows < compute_units && s > 1 && s <= kDoubleMaxSpans) {
+    const int64_t by_width = cols / kMinSpanCols;
+    s = 2 * s <= by_width ? 2 * s : (by_width > s ? by_width : s);
+  }
   if (k <= kNarrowMaxK && s > kMinNarrowSpans) {
     int64_t t = cols / kNarrowSpanCols;
     if (t < kMinNarrowSpans) t = kMinNarrowSpans;
