@@ -131,6 +131,7 @@ def test_plan():
     assert tk.plan_spans(128, 8192, 32) == 2         # no narrower than 4096 columns
     assert tk.plan_spans(128, 12288, 32) == 3
     assert tk.plan_spans(256, 151936, 64) == 1
+    assert tk.plan_spans(128, 98592, 128) == 4         # k > 64 doubles too
     for rows in (1, 3, 15, 64, 255, 256, 1000):
         for cols in (0, 1, 4095, 4096, 70000, 151936, 248320, 600000):
             s = tk.plan_spans(rows, cols, 16)

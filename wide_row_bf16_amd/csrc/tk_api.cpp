@@ -209,22 +209,30 @@ constexpr int64_t kNarrowSpanCols = 12288;
 constexpr int64_t kMinNarrowSpans = 8;
 constexpr int32_t kNarrowMaxK = 32;
 // Where the CU count asks for at most kDoubleMaxSpans spans (a third of the
-// CU count of rows or more, but fewer rows than CUs), the 16-bit scan takes
-// twice that many: two or more workgroups per CU, so one workgroup's fixed
+// CU count of rows or more, but fewer rows than CUs), the scans take twice
+// that many: two or more workgroups per CU, so one workgroup's fixed
 // chain (first load, floors, merges, fold) runs while another streams.
 // Measured per call, alternated rounds on one box (N(0, 2) rows): 96 x 98592
 // 16.6 us at 6 spans against 19.4 at 3; 128 x 98592 17.6 against 21.5;
 // 128 x 151936 at k = 64 23.4 against 30.3; 192 x 98592 19.3 against 22.8;
 // 224 x 98592 20.9 against 23.1.  At 64 rows (4 spans) doubling gained on
 // such rows but lost 0.4 us on rows of mixed ties and non-finite values.
+// The k > 64 and fp32 scans gain the same way: 128 x 98592 at k = 128
+// 24.6 us at 4 spans against 26.9 at 2 (fp32: 29.0 against 37.3);
+// 192 x 151936 at k = 256 36.8 against 42.8.
 constexpr int64_t kDoubleMaxSpans = 3;
 
-int32_t plan_scan16(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
-  int64_t s = plan(rows, cols, compute_units);
+int32_t doubled(int64_t rows, int64_t cols, int32_t spans, int32_t compute_units) {
+  int64_t s = spans;
   if (rows < compute_units && s > 1 && s <= kDoubleMaxSpans) {
     const int64_t by_width = cols / kMinSpanCols;
     s = 2 * s <= by_width ? 2 * s : (by_width > s ? by_width : s);
   }
+  return (int32_t)s;
+}
+
+int32_t plan_scan16(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
+  int64_t s = doubled(rows, cols, plan(rows, cols, compute_units), compute_units);
   if (k <= kNarrowMaxK && s > kMinNarrowSpans) {
     int64_t t = cols / kNarrowSpanCols;
     if (t < kMinNarrowSpans) t = kMinNarrowSpans;
@@ -520,7 +528,7 @@ tk_status run_argmax(int64_t rows, int64_t cols, int64_t stride, const uint16_t 
 constexpr int32_t kWideMaxAutoSpans = 12;
 
 int32_t plan_wide(int64_t rows, int64_t cols, int32_t compute_units) {
-  int32_t spans = plan(rows, cols, compute_units);
+  int32_t spans = doubled(rows, cols, plan(rows, cols, compute_units), compute_units);
   if (spans > kWideMaxAutoSpans) spans = kWideMaxAutoSpans;
   if (spans < (int32_t)min_spans(cols)) spans = (int32_t)min_spans(cols);
   return spans;
@@ -971,7 +979,7 @@ tk_status run32(int64_t rows, int64_t cols, int64_t stride, int32_t k, const uin
   if (k == 1 && !general && (forced > 0 || rows < device_cus(dev)))  // as for bf16: few rows or a forced split
     return run_argmax32(rows, cols, stride, in, out_idx, out_val, out_count, out_nonfinite, stream, dev,
                         forced > 0 ? forced : plan_argmax32(rows, cols, device_cus(dev)));
-  int32_t spans = forced > 0 ? forced : plan(rows, cols, device_cus(dev));
+  int32_t spans = forced > 0 ? forced : doubled(rows, cols, plan(rows, cols, device_cus(dev)), device_cus(dev));
   if (spans > kMergeGroup) spans = kMergeGroup;
   if (k > kMaxK && forced == 0 && spans > kWideMaxAutoSpans) spans = kWideMaxAutoSpans;
   // k > 64: the multi-register scan, with the same arguments and scratch
