@@ -132,6 +132,12 @@ def test_plan():
     assert tk.plan_spans(128, 12288, 32) == 3
     assert tk.plan_spans(256, 151936, 64) == 1
     assert tk.plan_spans(128, 98592, 128) == 4         # k > 64 doubles too
+    # 1 to 5 rows: up to 16 spans
+    assert tk.plan_spans(1, 151936, 32) == 16
+    assert tk.plan_spans(3, 98592, 32) == 16
+    assert tk.plan_spans(5, 248320, 64) == 16
+    assert tk.plan_spans(6, 98592, 32) == 8
+    assert tk.plan_spans(2, 40000, 16) == 9          # no narrower than 4096 columns
     for rows in (1, 3, 15, 64, 255, 256, 1000):
         for cols in (0, 1, 4095, 4096, 70000, 151936, 248320, 600000):
             s = tk.plan_spans(rows, cols, 16)

@@ -23,6 +23,10 @@ CASES = [
     (15, 49152, 32, "normal"),         # 8 spans at k <= 32
     (15, 151936, 20, "neginf_one_finite"),
     (15, 98592, 64, "normal"),         # k = 64 keeps 12
+    (3, 98592, 32, "normal"),          # 1 to 5 rows: 16 spans
+    (1, 151936, 32, "few_levels"),
+    (4, 248320, 20, "nan_sprinkled"),
+    (2, 40000, 64, "posinf_many"),
 ]
 
 

@@ -231,7 +231,27 @@ int32_t doubled(int64_t rows, int64_t cols, int32_t spans, int32_t compute_units
   return (int32_t)s;
 }
 
+// On so few rows that 12 spans fill under a quarter of the CUs (1 to 5 rows
+// on 256 CUs), the 16-bit scan takes up to kTinyMaxSpans: the fold's one
+// extra merge costs less than the shorter shares save.  Measured per call,
+// alternated rounds on one box (N(0, 2) rows), 16 spans against the plan of
+// 8 or 12: 1 x 151936 k = 32 12.75 against 13.15 us; 2 x 151936 k = 64 13.71
+// against 14.18; 3 x 98592 k = 32 12.11 against 12.31; 4 x 248320 k = 20
+// 14.09 against 14.89; 5 x 98592 12.13 against 12.44; 1 x 98592 k = 8 10.99
+// against 11.11 (20 spans: faster still on the wider rows, slower on 98592
+// columns).
+constexpr int64_t kTinyMaxSpans = 16;
+
 int32_t plan_scan16(int64_t rows, int64_t cols, int32_t k, int32_t compute_units) {
+  if (rows > 0 && cols > 0 && rows * kMaxAutoSpans * 4 < compute_units) {
+    int64_t t = (compute_units + rows - 1) / rows;
+    const int64_t by_width = cols / kMinSpanCols;
+    if (t > by_width) t = by_width;
+    if (t > kTinyMaxSpans) t = kTinyMaxSpans;
+    const int64_t need = min_spans(cols);
+    if (t < need) t = need;
+    return (int32_t)(t < 1 ? 1 : t);
+  }
   int64_t s = doubled(rows, cols, plan(rows, cols, compute_units), compute_units);
   if (k <= kNarrowMaxK && s > kMinNarrowSpans) {
     int64_t t = cols / kNarrowSpanCols;
